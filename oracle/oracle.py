@@ -1,0 +1,210 @@
+"""ctypes front end of the C++ fp64 oracle (``kq_oracle.cpp``).
+
+TEST INFRASTRUCTURE ONLY.  Each function mirrors one C entry point; the
+arithmetic lives in the C++ file, whose header names the passages it follows.
+Parity unpinned: nothing on the pages prints numeric values for this path, so
+the oracle is pinned by closed forms, invariants and brute force in the tests.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle_kq.so")
+SOURCES = [os.path.join(HERE, "kq_oracle.cpp")]
+
+BF16, FP32 = 0, 1
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with g++ (-O2, no FMA contraction) into liboracle_kq.so."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+           "-shared", "-pthread", "-Wall", "-Wextra", "-o", tmp] + SOURCES
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        L.oq_factor.argtypes = [D, D, D, P]
+        L.oq_factor_inverse.argtypes = [D, D, D, P]
+        L.oq_kron.argtypes = [P, I, I, P, I, I, P]
+        L.oq_expand.argtypes = [P, I64, I, P]
+        L.oq_det.argtypes = [P, I]
+        L.oq_det.restype = D
+        L.oq_transform_dense.argtypes = [P, I, I64, I64, I64, P, P]
+        L.oq_transform_factored.argtypes = [P, I, I64, I64, I64, P, P]
+        L.oq_scale_exp.argtypes = [D]
+        L.oq_e2m1_code.argtypes = [D, I]
+        L.oq_e2m1_value.argtypes = [I, I]
+        L.oq_e2m1_value.restype = D
+        L.oq_encode.argtypes = [P, I64, I64, P, I64, P, I64]
+        L.oq_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
+        L.oq_sq_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
+        L.oq_classify.argtypes = [P, I, I64, I64, I64, P, I, D, P, I64, P, I64, P, I64, P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def _x_info(x: np.ndarray):
+    """(dtype code, rows, ldx) of an input held as uint16 bf16 bits or float32."""
+    if x.dtype == np.uint16:
+        dt = BF16
+    elif x.dtype == np.float32:
+        dt = FP32
+    else:
+        raise TypeError("oracle input must be uint16 (bf16 bits) or float32")
+    if x.ndim != 2 or x.strides[1] != x.itemsize or x.strides[0] % x.itemsize:
+        raise ValueError("oracle input must be a 2-D array with unit column stride")
+    return dt, x.shape[0], x.strides[0] // x.itemsize
+
+
+def factor(l, u, v):
+    F = np.zeros(4, np.float64)
+    lib().oq_factor(l, u, v, _ptr(F))
+    return F.reshape(2, 2)
+
+
+def factor_inverse(l, u, v):
+    F = np.zeros(4, np.float64)
+    lib().oq_factor_inverse(l, u, v, _ptr(F))
+    return F.reshape(2, 2)
+
+
+def kron(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    A = np.ascontiguousarray(A, np.float64)
+    B = np.ascontiguousarray(B, np.float64)
+    C = np.zeros((A.shape[0] * B.shape[0], A.shape[1] * B.shape[1]), np.float64)
+    lib().oq_kron(_ptr(A), A.shape[0], A.shape[1], _ptr(B), B.shape[0], B.shape[1], _ptr(C))
+    return C
+
+
+def expand(params: np.ndarray, inverse: bool = False) -> np.ndarray:
+    p = np.ascontiguousarray(params, np.float32)
+    nb = p.shape[0]
+    assert p.shape == (nb, 5, 3)
+    T = np.zeros((nb, 32, 32), np.float64)
+    _check(lib().oq_expand(_ptr(p), nb, int(inverse), _ptr(T)), "expand")
+    return T
+
+
+def det(A: np.ndarray) -> float:
+    A = np.ascontiguousarray(A, np.float64)
+    return lib().oq_det(_ptr(A), A.shape[0])
+
+
+def transform_dense(x: np.ndarray, T: np.ndarray) -> np.ndarray:
+    dt, rows, ldx = _x_info(x)
+    d = x.shape[1]
+    Tm = np.ascontiguousarray(T, np.float64)
+    y = np.zeros((rows, d), np.float64)
+    _check(lib().oq_transform_dense(_ptr(x), dt, rows, d, ldx, _ptr(Tm), _ptr(y)), "transform_dense")
+    return y
+
+
+def transform_factored(x: np.ndarray, params: np.ndarray) -> np.ndarray:
+    dt, rows, ldx = _x_info(x)
+    d = x.shape[1]
+    p = np.ascontiguousarray(params, np.float32)
+    y = np.zeros((rows, d), np.float64)
+    _check(lib().oq_transform_factored(_ptr(x), dt, rows, d, ldx, _ptr(p), _ptr(y)), "transform_factored")
+    return y
+
+
+def scale_exp(amax: float) -> int:
+    return lib().oq_scale_exp(float(amax))
+
+
+def e2m1_code(y: float, e: int) -> int:
+    return lib().oq_e2m1_code(float(y), int(e))
+
+
+def e2m1_value(code: int, e: int) -> float:
+    return lib().oq_e2m1_value(int(code), int(e))
+
+
+def encode(y: np.ndarray):
+    y = np.ascontiguousarray(y, np.float64)
+    rows, d = y.shape
+    q = np.zeros((rows, d // 2), np.uint8)
+    s = np.zeros((rows, d // 32), np.uint8)
+    _check(lib().oq_encode(_ptr(y), rows, d, _ptr(q), d // 2, _ptr(s), d // 32), "encode")
+    return q, s
+
+
+def quantize(x: np.ndarray, params: np.ndarray, want_y: bool = False, nthreads: int = 0):
+    """Returns (q [rows, d/2] uint8, s [rows, d/32] uint8, y fp64 or None)."""
+    dt, rows, ldx = _x_info(x)
+    d = x.shape[1]
+    p = np.ascontiguousarray(params, np.float32)
+    assert p.shape == (d // 32, 5, 3)
+    q = np.zeros((rows, d // 2), np.uint8)
+    s = np.zeros((rows, d // 32), np.uint8)
+    y = np.zeros((rows, d), np.float64) if want_y else None
+    rc = lib().oq_quantize(_ptr(x), dt, rows, d, ldx, _ptr(p), _ptr(q), d // 2, _ptr(s), d // 32,
+                           _ptr(y) if want_y else None, nthreads)
+    _check(rc, "quantize")
+    return q, s, y
+
+
+def sq_quantize(x: np.ndarray, mult: np.ndarray, want_y: bool = False, nthreads: int = 0):
+    dt, rows, ldx = _x_info(x)
+    d = x.shape[1]
+    m = np.ascontiguousarray(mult, np.float32)
+    assert m.shape == (d,)
+    q = np.zeros((rows, d // 2), np.uint8)
+    s = np.zeros((rows, d // 32), np.uint8)
+    y = np.zeros((rows, d), np.float64) if want_y else None
+    rc = lib().oq_sq_quantize(_ptr(x), dt, rows, d, ldx, _ptr(m), _ptr(q), d // 2, _ptr(s), d // 32,
+                              _ptr(y) if want_y else None, nthreads)
+    _check(rc, "sq_quantize")
+    return q, s, y
+
+
+STAT_NAMES = ("exact", "excused", "unexcused", "excused_scale_blocks", "unexcused_scale_blocks",
+              "prequant_violations", "max_norm_prequant_err", "first_unexcused")
+
+
+def classify(x: np.ndarray, y_o: np.ndarray, q: np.ndarray, s: np.ndarray, tol_mode: int = 0,
+             tol_coef: float = 1e-5, y_c: np.ndarray | None = None) -> dict:
+    """Parity accounting of candidate (q, s[, y_c]) against the oracle's y_o."""
+    dt, rows, ldx = _x_info(x)
+    d = x.shape[1]
+    y_o = np.ascontiguousarray(y_o, np.float64)
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.uint8)
+    assert y_o.shape == (rows, d) and q.shape == (rows, d // 2) and s.shape == (rows, d // 32)
+    if y_c is not None:
+        y_c = np.ascontiguousarray(y_c, np.float32)
+        assert y_c.shape == (rows, d)
+    st = np.zeros(8, np.float64)
+    rc = lib().oq_classify(_ptr(x), dt, rows, d, ldx, _ptr(y_o), tol_mode, tol_coef,
+                           _ptr(q), d // 2, _ptr(s), d // 32,
+                           _ptr(y_c) if y_c is not None else None, d, _ptr(st))
+    _check(rc, "classify")
+    out = dict(zip(STAT_NAMES, st.tolist()))
+    out["elements"] = rows * d
+    return out

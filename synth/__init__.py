@@ -1,0 +1,11 @@
+"""Seeded synthetic inputs for the KroQuant quantizer (shared by tests, bench, smoke).
+
+This package draws activations, factor parameters and SmoothQuant multipliers.
+It holds none of the quantizer's arithmetic and imports neither the oracle nor
+the GPU library.
+"""
+from .configs import CONFIGS, Config, get_config  # noqa: F401
+from .gen import (  # noqa: F401
+    bf16_bits_from_f32, f32_from_bf16_bits, make_activations, make_params, make_identity_params,
+    make_sq_mult, make_inputs,
+)

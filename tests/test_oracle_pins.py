@@ -1,0 +1,288 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Sources: KroQuant abstract (arXiv 2607.21446) and its researchpod summary (method
+paragraph) for the block transform; OCP MX v1.0 for MXFP4.  Each test names
+the fact it checks.  No GPU is used.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+def rand_params(nb, seed):
+    return synth.make_params(nb, np.random.default_rng(seed))
+
+
+def f32_block(vals, d=32):
+    x = np.zeros((1, d), np.float32)
+    x[0, : len(vals)] = vals
+    return x
+
+
+# ---------------------------------------------------------------- factors / T_b
+
+def test_factor_is_l_times_u(oq):
+    # L = [[1,0],[l,1]], U = [[u,v],[0,1/u]]  ->  L U = [[u, v],[l u, l v + 1/u]]
+    l, u, v = 0.7, 1.9, -0.35
+    F = oq.factor(l, u, v)
+    assert np.allclose(F, [[u, v], [l * u, l * v + 1 / u]], rtol=0, atol=1e-15)
+    Fi = oq.factor_inverse(l, u, v)
+    assert np.allclose(F @ Fi, np.eye(2), atol=1e-14)
+
+
+def test_kron_matches_numpy(oq):
+    rng = np.random.default_rng(5)
+    A, B = rng.normal(size=(2, 3)), rng.normal(size=(4, 2))
+    assert np.array_equal(oq.kron(A, B), np.kron(A, B))
+
+
+def test_expand_is_kron_product_in_order(oq):
+    # T_b = F1 (x) F2 (x) F3 (x) F4 (x) F5 (researchpod summary, method paragraph),
+    # checked against numpy.kron of the closed-form factors.
+    p = rand_params(3, 11)
+    T = oq.expand(p)
+    for b in range(3):
+        Fs = [np.array([[u, v], [l * u, l * v + 1.0 / u]], np.float64)
+              for (l, u, v) in p[b].astype(np.float64)]
+        ref = Fs[0]
+        for F in Fs[1:]:
+            ref = np.kron(ref, F)
+        np.testing.assert_allclose(T[b], ref, rtol=1e-14, atol=1e-14)
+
+
+def test_p1_unit_determinant(oq):
+    # det F = u (l v + 1/u) - v l u = 1 and det(A (x) B) = det(A)^m det(B)^n  ->  det T_b = 1
+    p = rand_params(64, 1)
+    T = oq.expand(p)
+    for b in range(64):
+        assert abs(oq.det(T[b]) - 1.0) <= 1e-12
+        assert abs(np.linalg.det(T[b]) - 1.0) <= 1e-10
+
+
+def test_p2_kron_of_inverses_is_inverse(oq):
+    # (F1 (x) ... (x) F5)^-1 = F1^-1 (x) ... (x) F5^-1 (the inverse goes to the weights)
+    p = rand_params(32, 2)
+    T, Ti = oq.expand(p), oq.expand(p, inverse=True)
+    for b in range(32):
+        err = np.abs(T[b] @ Ti[b] - np.eye(32)).max()
+        assert err <= 1e-12 * max(1.0, np.abs(T[b]).max() * np.abs(Ti[b]).max())
+
+
+def test_p6_parameter_count_below_half_of_per_channel():
+    # abstract: fewer than half the parameters of per-channel scaling.
+    per_block = 5 * 3  # five factors, three free parameters (l, u, v) each
+    assert per_block / 32 < 0.5
+    assert 5 * 4 / 32 > 0.5  # a general 2x2 factor would not satisfy the claim
+
+
+def test_p5_dense_equals_factored(oq):
+    rng = np.random.default_rng(3)
+    p = rand_params(4, 3)
+    x = rng.normal(size=(8, 128)).astype(np.float32) * 10
+    yd = oq.transform_dense(x, oq.expand(p))
+    yf = oq.transform_factored(x, p)
+    # bound the rounding by the absolute dense sum
+    T = oq.expand(p)
+    bound = np.zeros_like(yd)
+    for b in range(4):
+        bound[:, 32 * b:32 * b + 32] = np.abs(x[:, 32 * b:32 * b + 32].astype(np.float64)) @ np.abs(T[b]).T
+    assert np.all(np.abs(yd - yf) <= 1e-12 * bound + 1e-300)
+
+
+def test_p10_single_factor_closed_forms(oq):
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=(3, 64)).astype(np.float32)
+    for k in range(5):
+        p = synth.make_identity_params(2)
+        l, u, v = 0.4, 1.7, -0.9
+        p[:, k] = (l, u, v)
+        l, u, v = (float(t) for t in p[0, k])  # the fp32 values the oracle reads
+        F = np.array([[u, v], [l * u, l * v + 1 / u]], np.float64)
+        y = oq.transform_dense(x, oq.expand(p))
+        st = 16 >> k  # F_{k+1} acts on bit 4 - k
+        ref = x.astype(np.float64).copy()
+        for i in range(64):
+            if (i % 32) & st:
+                continue
+            a, c = x[:, i].astype(np.float64), x[:, i + st].astype(np.float64)
+            ref[:, i] = F[0, 0] * a + F[0, 1] * c
+            ref[:, i + st] = F[1, 0] * a + F[1, 1] * c
+        np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------ MXFP4 encode
+
+def load_golden():
+    path = os.path.join(HERE, "golden", "worked_examples.txt")
+    ex, cur = [], None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, _, rest = line.partition(" ")
+        if key == "example":
+            cur = {"name": rest}
+        elif key == "params":
+            cur["params"] = np.array(rest.split(), np.float32).reshape(1, 5, 3)
+        elif key == "x":
+            cur["x"] = np.array(rest.split(), np.float32).reshape(1, 32)
+        elif key == "S":
+            cur["S"] = int(rest)
+        elif key == "Q":
+            cur["Q"] = [int(c, 16) for c in rest.split()]
+        elif key == "end":
+            ex.append(cur)
+    return ex
+
+
+GOLDEN = load_golden()
+
+
+@pytest.mark.parametrize("ex", GOLDEN, ids=[e["name"] for e in GOLDEN])
+def test_p9_worked_examples(oq, ex):
+    q, s, _ = oq.quantize(ex["x"], ex["params"])
+    assert int(s[0, 0]) == ex["S"]
+    codes = [(q[0, i // 2] >> (4 * (i & 1))) & 0xF for i in range(32)]
+    assert codes == ex["Q"]
+
+
+def test_scale_rule_points(oq):
+    # e = floor(log2 amax) - 2, clamped to [-127, 127]; zero -> -127; NaN/Inf -> marker
+    assert oq.scale_exp(0.0) == -127
+    assert oq.scale_exp(1.0) == -2
+    assert oq.scale_exp(np.nextafter(1.0, 0)) == -3
+    assert oq.scale_exp(6.0) == 0 and oq.scale_exp(8.0) == 1 and oq.scale_exp(7.999) == 0
+    assert oq.scale_exp(2.0 ** -200) == -127
+    assert oq.scale_exp(2.0 ** 200) == 127
+    assert oq.scale_exp(float("inf")) == 128 and oq.scale_exp(float("nan")) == 128
+
+
+def test_p4_e2m1_exhaustive_against_argmin(tmp_path):
+    """Every finite fp32 value, plus fp64 ulps around every midpoint, against an
+    independently written arg-min over the E2M1 grid (tests/native/e2m1_sweep.c)."""
+    exe = tmp_path / "e2m1_sweep"
+    lib_dir = os.path.join(ROOT, "oracle")
+    subprocess.run(["gcc", "-O2", "-o", str(exe), os.path.join(HERE, "native", "e2m1_sweep.c"),
+                    "-L", lib_dir, "-l:liboracle_kq.so", f"-Wl,-rpath,{lib_dir}", "-lpthread", "-lm"],
+                   check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "sweep_bad=0" in res.stdout and "ulp_bad=0" in res.stdout
+
+
+def test_p3_identity_factors_reduce_to_plain_mxfp4(oq):
+    # T_b = I: the quantizer is plain MXFP4 of x, bit for bit.
+    cfg = synth.get_config("pixart")
+    x, _, _ = synth.make_inputs(cfg, rows=64)
+    q, s, y = oq.quantize(x, synth.make_identity_params(cfg.nb), want_y=True)
+    xf = synth.f32_from_bf16_bits(x).astype(np.float64)
+    assert np.array_equal(y, xf)
+    q2, s2 = oq.encode(xf)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+def test_p7_power_of_two_shifts_scale_only(oq):
+    rng = np.random.default_rng(7)
+    x = rng.normal(size=(16, 96)).astype(np.float32)
+    p = rand_params(3, 7)
+    q0, s0, _ = oq.quantize(x, p)
+    for k in (-20, -3, 1, 5, 20):
+        qk, sk, _ = oq.quantize((x * np.float32(2.0 ** k)).astype(np.float32), p)
+        assert np.array_equal(qk, q0)
+        assert np.array_equal(sk.astype(int), s0.astype(int) + k)
+
+
+def test_p8_negation_flips_sign_bits(oq):
+    rng = np.random.default_rng(8)
+    x = rng.normal(size=(16, 96)).astype(np.float32)
+    p = rand_params(3, 8)
+    q0, s0, y0 = oq.quantize(x, p, want_y=True)
+    q1, s1, _ = oq.quantize(-x, p)
+    assert np.array_equal(s0, s1)
+    assert np.all(y0 != 0)  # no zeros, so every nibble's sign flips
+    assert np.array_equal(q1, q0 ^ 0x88)
+
+
+def test_p11_row_independence_and_pitch(oq):
+    cfg = synth.get_config("tiny")
+    x, p, _ = synth.make_inputs(cfg, rows=40)
+    q, s, _ = oq.quantize(x, p)
+    for rows in (0, 1, 31, 33):
+        qr, sr, _ = oq.quantize(np.ascontiguousarray(x[:rows]), p)
+        assert np.array_equal(qr, q[:rows]) and np.array_equal(sr, s[:rows])
+    wide = np.zeros((40, cfg.d + 64), np.float32)
+    wide[:, : cfg.d] = x
+    wide[:, cfg.d:] = 1e30  # must never be read
+    qw, sw, _ = oq.quantize(wide[:, : cfg.d], p)
+    assert np.array_equal(qw, q) and np.array_equal(sw, s)
+
+
+def test_nonfinite_block_marker(oq):
+    x = f32_block([1.0, 2.0])
+    x[0, 5] = np.nan
+    q, s, _ = oq.quantize(x, synth.make_identity_params(1))
+    assert s[0, 0] == 0xFF and not q.any()
+
+
+def test_sq_oracle_reduces(oq):
+    rng = np.random.default_rng(9)
+    x = rng.normal(size=(8, 64)).astype(np.float32)
+    ones = np.ones(64, np.float32)
+    q1, s1, _ = oq.sq_quantize(x, ones)
+    q2, s2, _ = oq.quantize(x, synth.make_identity_params(2))
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+    q3, s3, _ = oq.sq_quantize(x, np.full(64, 0.25, np.float32))
+    assert np.array_equal(q3, q1) and np.array_equal(s3.astype(int), s1.astype(int) - 2)
+    # per-channel multiply: channel c only sees mult[c]
+    m = np.exp(rng.normal(size=64)).astype(np.float32)
+    _, _, y = oq.sq_quantize(x, m, want_y=True)
+    assert np.array_equal(y, x.astype(np.float64) * m.astype(np.float64))
+
+
+# ---------------------------------------------------------------- parity rule
+
+def test_classify_counts_planted_mismatches(oq):
+    """The parity accounting itself: exact outputs pass; a code moved by one step
+    at a value far from any boundary is unexcused; one at a value within tol of a
+    boundary is excused; a scale off by one away from a power of two is unexcused."""
+    x = f32_block([7.9, 6, 5, 3.5, 2.5, 1.75, 1.25, 0.75, 0.25, -0.25, 3.0, 1.0])
+    p = synth.make_identity_params(1)
+    q, s, y = oq.quantize(x, p, want_y=True)
+    st = oq.classify(x, y, q, s, 0, 1e-5)
+    assert st["exact"] == 32 and st["unexcused"] == 0 and st["excused"] == 0
+    # channel 2 holds 5.0, exactly on the 4|6 boundary: code 7 is excusable
+    q2 = q.copy()
+    q2[0, 1] = (q2[0, 1] & 0xF0) | 7
+    st = oq.classify(x, y, q2, s, 0, 1e-5)
+    assert st["excused"] == 1 and st["unexcused"] == 0
+    # channel 10 holds 3.0, far from any boundary: code 6 is not excusable
+    q3 = q.copy()
+    q3[0, 5] = (q3[0, 5] & 0xF0) | 6
+    st = oq.classify(x, y, q3, s, 0, 1e-5)
+    assert st["unexcused"] == 1 and st["first_unexcused"] == 10
+    # scale off by one with amax 7.9 (not near 8): unexcused block
+    s4 = s.copy()
+    s4[0, 0] += 1
+    st = oq.classify(x, y, q, s4, 0, 1e-5)
+    assert st["unexcused_scale_blocks"] == 1 and st["unexcused"] == 32
+    # amax within tol of 8: the higher scale is excused, codes judged at that scale
+    xe = f32_block([np.nextafter(np.float32(8), np.float32(0)), 1.0])
+    qe, se, ye = oq.quantize(xe, p, want_y=True)
+    assert se[0, 0] == 127
+    xs = f32_block([8.0, 1.0])
+    qs_, ss_, _ = oq.quantize(xs, p)
+    st = oq.classify(xe, ye, qs_, ss_, 0, 1e-5)
+    assert st["excused_scale_blocks"] == 1 and st["unexcused"] == 0 and st["excused"] == 32
+    # pre-quant check
+    yc = y.astype(np.float32).copy()
+    yc[0, 3] += 1e-3
+    st = oq.classify(x, y, q, s, 0, 1e-5, y_c=yc)
+    assert st["prequant_violations"] == 1
+    assert abs(st["max_norm_prequant_err"] - 1e-3 / 7.9) < 1e-6

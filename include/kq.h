@@ -1,0 +1,145 @@
+/*
+ * kq.h — C ABI of the KroQuant online activation quantizer for AMD gfx950
+ * (MI350 / MI355X).
+ *
+ * What it computes.  For every token row t of a linear-layer input X[T][d] and
+ * every 32-channel block b (channels 32b .. 32b+31), the block is multiplied by
+ * its own invertible 32x32 transform T_b and the result is encoded as MXFP4:
+ * 32 E2M1 codes sharing one E8M0 scale.
+ *   - KroQuant abstract (arXiv 2607.21446): one learned Kronecker-structured
+ *     invertible transform per 32-element activation block, applied online
+ *     before W4A4 (MXFP4) quantization; its inverse is folded into the weights;
+ *     per-channel scaling (SmoothQuant) is the cheap comparison transform.
+ *   - KroQuant researchpod summary, method paragraph: T_b is the Kronecker
+ *     product of five 2x2 unit-determinant LU-decomposed factors.
+ *   - OCP Microscaling Formats (MX) v1.0: MXFP4 element and scale encodings.
+ *
+ * Conventions fixed by this library (the pages leave them open):
+ *   factor   F = L*U, L = [[1,0],[l,1]], U = [[u,v],[0,1/u]]   (det F = 1)
+ *   params   float32 [nb][5][3] = (l, u, v) for F1..F5 of each block
+ *   T_b      = F1 (x) F2 (x) F3 (x) F4 (x) F5; F1 acts on bit 4 of the within-block
+ *            index i (stride 16), F5 on bit 0 (stride 1)
+ *   y_b      = T_b * x_b   (so a consumer's weights take W_b * T_b^-1)
+ *   scale    e = clamp(floor(log2(max_i |y_i|)) - 2, -127, 127), byte S = e + 127;
+ *            an all-zero block gives S = 0; a block holding NaN or Inf gives
+ *            S = 0xFF and all-zero codes
+ *   codes    |y_i| / 2^e rounded to the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}
+ *            (midpoints to the even code, above 6 saturates to 6); bit 3 is the
+ *            sign of y_i, so a negative value that rounds to zero encodes as 0x8
+ *   layout   Q: uint8 [T][ldq], byte 16b + i/2 of row t holds channel 32b+i, even i
+ *            in the low nibble; S: uint8 [T][lds], byte b of row t is the block's
+ *            E8M0 scale; X and Q/S are row-major with the given row pitches
+ *
+ * Calling rules shared by every entry point:
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or synchronizes; each call enqueues work on
+ *     `stream` (a hipStream_t passed as void*, NULL = the null stream) and
+ *     returns without waiting.
+ *   - Arguments are checked on the host before any HIP call; a rejected call
+ *     returns a negative kq_status and enqueues nothing.  KQ_ERR_HIP means a
+ *     launch failed; kq_last_hip_error() gives the hipError_t (per thread).
+ *     Nothing is printed and no exception crosses the ABI.
+ *   - rows == 0 is a no-op that returns KQ_OK.  d must be a positive multiple of
+ *     32.  x, q and their row pitches (in bytes) must be 16-byte aligned.
+ *   - Factor parameters must be finite with u != 0; otherwise the output is
+ *     unspecified (checking would cost a device pass).  Inputs are expected to be
+ *     finite; the NaN/Inf scale rule above is best effort.
+ *   - Calls are reentrant and thread-safe; the only global state is a per-device
+ *     cache of the compute-unit count.
+ */
+#ifndef KQ_H
+#define KQ_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KQ_OK = 0,
+  KQ_ERR_NULL = -1,     /* a required pointer is NULL                       */
+  KQ_ERR_SHAPE = -2,    /* negative rows, d not a positive multiple of 32,
+                           a pitch smaller than the row, or nb mismatch      */
+  KQ_ERR_ALIGN = -3,    /* x, q (or a pitch in bytes) not 16-byte aligned   */
+  KQ_ERR_DTYPE = -4,    /* unknown input dtype                              */
+  KQ_ERR_FORMAT = -5,   /* unknown transform format, or one the variant
+                           cannot consume                                    */
+  KQ_ERR_VARIANT = -6,  /* unknown variant                                  */
+  KQ_ERR_HIP = -7       /* a HIP call failed                                */
+} kq_status;
+
+typedef enum { KQ_BF16 = 0, KQ_FP32 = 1 } kq_dtype;
+
+/* Transform formats.  Element counts per block: PARAMS 15 floats, DENSE_F32
+ * 1024 floats, DENSE_BF16X3 3 x 1024 bf16. */
+typedef enum {
+  KQ_T_PARAMS = 0,        /* float32 [nb][5][3] (l,u,v): the factors themselves   */
+  KQ_T_DENSE_F32 = 1,     /* float32 [nb][32][32]: T_b[i][j] row-major            */
+  KQ_T_DENSE_BF16X3 = 2   /* bf16 [3][nb][32][32]: hi, mid, lo with
+                             hi + mid + lo == fp32(T_b) (each the bf16 rounding of
+                             what the previous parts leave)                       */
+} kq_tfmt;
+
+typedef enum {
+  KQ_AUTO = 0,       /* BUTTERFLY for KQ_T_PARAMS, MFMA for KQ_T_DENSE_BF16X3     */
+  KQ_BUTTERFLY = 1,  /* fp32 in-register factored transform; needs KQ_T_PARAMS   */
+  KQ_MFMA = 2        /* per-block 32x32 bf16 matrix-core product with fp32
+                        accumulation over the 3-way split T; needs
+                        KQ_T_DENSE_BF16X3                                         */
+} kq_variant;
+
+/* Expand factor parameters into a transform format (the work the abstract
+ * describes as folding the block structure into small GEMMs).
+ *   params  device float32 [nb][5][3]
+ *   nb      number of 32-channel blocks (>= 0; 0 is a no-op)
+ *   tfmt    KQ_T_DENSE_F32 or KQ_T_DENSE_BF16X3 (KQ_T_PARAMS is rejected: it
+ *           needs no expansion)
+ *   t_out   device buffer of the format's size (see kq_tfmt)
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE (nb < 0), KQ_ERR_FORMAT, KQ_ERR_HIP. */
+int kq_expand_factors(const float* params, int64_t nb, int tfmt, void* t_out, void* stream);
+
+/* Transform each 32-channel block of every row and encode it as MXFP4.
+ *   x       device [rows][ldx] of dtype (bf16 held as 16-bit words, or float32)
+ *   rows    token rows (>= 0); d channels (multiple of 32); ldx row pitch in
+ *           elements (>= d)
+ *   t, tfmt the transform in one of the kq_tfmt formats, nb = d/32 blocks
+ *   q       device uint8 [rows][ldq], ldq >= d/2 bytes
+ *   s       device uint8 [rows][lds], lds >= d/32 bytes
+ *   variant kq_variant
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_DTYPE, KQ_ERR_FORMAT,
+ *         KQ_ERR_VARIANT, KQ_ERR_HIP. */
+int kq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                const void* t, int tfmt, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                int variant, void* stream);
+
+/* SmoothQuant baseline on the same memory skeleton: y[t][c] = x[t][c] * mult[c]
+ * (mult = 1/s_c in float32, the per-channel smoothing the abstract compares
+ * against), then the same MXFP4 encoding and layout as kq_quantize.
+ *   mult    device float32 [d]
+ * Errors: as kq_quantize (KQ_ERR_FORMAT and KQ_ERR_VARIANT never occur). */
+int sq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                const float* mult, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                void* stream);
+
+/* Validation entry: kq_quantize from the same kernels, additionally writing the
+ * float32 pre-quantization values y into y [rows][ldy] (ldy >= d elements, any
+ * 4-byte-aligned pointer).  Slower; not for production use. */
+int kq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                       const void* t, int tfmt, uint8_t* q, int64_t ldq, uint8_t* s,
+                       int64_t lds, int variant, float* y, int64_t ldy, void* stream);
+
+/* Same for the SmoothQuant baseline. */
+int sq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                       const float* mult, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                       float* y, int64_t ldy, void* stream);
+
+/* Static text for a kq_status value (never NULL). */
+const char* kq_status_string(int status);
+
+/* hipError_t of this thread's last KQ_ERR_HIP (0 if none). */
+int kq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

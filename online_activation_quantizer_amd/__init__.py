@@ -1,0 +1,11 @@
+"""KroQuant online activation quantizer for AMD gfx950 (MI350 / MI355X).
+
+The compute path is the HIP library ``libkq.so`` (C ABI in ``include/kq.h``);
+this package only marshals arguments to it.  There is no CPU fallback: when
+the library is missing or fails to load, every call raises.
+"""
+from .kq import (  # noqa: F401
+    KQ_AUTO, KQ_BF16, KQ_BUTTERFLY, KQ_FP32, KQ_MFMA, KQ_T_DENSE_BF16X3, KQ_T_DENSE_F32,
+    KQ_T_PARAMS, KQError, STATUS, kq_expand_factors, kq_quantize, kq_transform_debug, lib,
+    sq_quantize, sq_transform_debug, expanded_numel, EXPORTED_SYMBOLS,
+)

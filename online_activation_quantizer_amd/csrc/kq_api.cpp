@@ -1,0 +1,185 @@
+// kq_api.cpp — the C ABI declared in include/kq.h: host-side argument checks,
+// variant dispatch and launches.  Every check runs before the first HIP call.
+#include "../../include/kq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+
+#include "kq_launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // 0 = not queried yet
+
+int fail_hip(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return KQ_ERR_HIP;
+}
+
+// Compute units of the current device (cached per device).
+int current_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e);
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return KQ_OK;
+    }
+  }
+  int c = 0;
+  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail_hip(e);
+  if (c < 1) c = 1;
+  if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return KQ_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int elem_size(int dtype) { return dtype == KQ_BF16 ? 2 : 4; }
+
+// Checks shared by the quantize entry points.
+int check_common(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                 const void* t, const uint8_t* q, int64_t ldq, const uint8_t* s, int64_t lds) {
+  if (dtype != KQ_BF16 && dtype != KQ_FP32) return KQ_ERR_DTYPE;
+  if (rows < 0 || d <= 0 || d % 32 != 0 || ldx < d || ldq < d / 2 || lds < d / 32)
+    return KQ_ERR_SHAPE;
+  if (d / 32 > INT32_MAX) return KQ_ERR_SHAPE;
+  if (rows == 0) return KQ_OK;
+  if (!x || !t || !q || !s) return KQ_ERR_NULL;
+  if (!aligned(x, 16) || (ldx * elem_size(dtype)) % 16 != 0 || !aligned(q, 16) || ldq % 16 != 0)
+    return KQ_ERR_ALIGN;
+  return KQ_OK;
+}
+
+int resolve_variant(int variant, int tfmt, int* out) {
+  if (tfmt != KQ_T_PARAMS && tfmt != KQ_T_DENSE_F32 && tfmt != KQ_T_DENSE_BF16X3)
+    return KQ_ERR_FORMAT;
+  switch (variant) {
+    case KQ_AUTO:
+      if (tfmt == KQ_T_PARAMS) *out = KQ_BUTTERFLY;
+      else if (tfmt == KQ_T_DENSE_BF16X3) *out = KQ_MFMA;
+      else return KQ_ERR_FORMAT;
+      return KQ_OK;
+    case KQ_BUTTERFLY:
+      if (tfmt != KQ_T_PARAMS) return KQ_ERR_FORMAT;
+      *out = KQ_BUTTERFLY;
+      return KQ_OK;
+    case KQ_MFMA:
+      if (tfmt != KQ_T_DENSE_BF16X3) return KQ_ERR_FORMAT;
+      *out = KQ_MFMA;
+      return KQ_OK;
+    default:
+      return KQ_ERR_VARIANT;
+  }
+}
+
+int quantize_impl(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, const void* t,
+                  int tfmt, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, int variant,
+                  float* y, int64_t ldy, bool debug, void* stream) {
+  int rc = check_common(x, dtype, rows, d, ldx, t, q, ldq, s, lds);
+  if (rc != KQ_OK) return rc;
+  int v = 0;
+  rc = resolve_variant(variant, tfmt, &v);
+  if (rc != KQ_OK) return rc;
+  if (debug) {
+    if (ldy < d) return KQ_ERR_SHAPE;
+    if (rows > 0 && !y) return KQ_ERR_NULL;
+    if (rows > 0 && !aligned(y, 4)) return KQ_ERR_ALIGN;
+  }
+  if (rows == 0) return KQ_OK;
+  if (!aligned(t, v == KQ_MFMA ? 16 : 4)) return KQ_ERR_ALIGN;
+  if (v == KQ_MFMA && dtype != KQ_BF16) return KQ_ERR_DTYPE;
+  kq::LaunchArgs a{x, dtype, rows, d, d / 32, ldx, t, q, ldq, s, lds, debug ? y : nullptr,
+                   ldy, stream, 0};
+  rc = current_cus(&a.cus);
+  if (rc != KQ_OK) return rc;
+  const hipError_t e = v == KQ_MFMA ? kq::launch_mfma(a) : kq::launch_butterfly(a);
+  return e == hipSuccess ? KQ_OK : fail_hip(e);
+}
+
+int sq_impl(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, const float* mult,
+            uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, float* y, int64_t ldy, bool debug,
+            void* stream) {
+  int rc = check_common(x, dtype, rows, d, ldx, mult, q, ldq, s, lds);
+  if (rc != KQ_OK) return rc;
+  if (debug) {
+    if (ldy < d) return KQ_ERR_SHAPE;
+    if (rows > 0 && !y) return KQ_ERR_NULL;
+    if (rows > 0 && !aligned(y, 4)) return KQ_ERR_ALIGN;
+  }
+  if (rows == 0) return KQ_OK;
+  if (!aligned(mult, 16)) return KQ_ERR_ALIGN;
+  kq::LaunchArgs a{x, dtype, rows, d, d / 32, ldx, mult, q, ldq, s, lds, debug ? y : nullptr,
+                   ldy, stream, 0};
+  rc = current_cus(&a.cus);
+  if (rc != KQ_OK) return rc;
+  const hipError_t e = kq::launch_sq(a);
+  return e == hipSuccess ? KQ_OK : fail_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kq_expand_factors(const float* params, int64_t nb, int tfmt, void* t_out, void* stream) {
+  if (tfmt != KQ_T_DENSE_F32 && tfmt != KQ_T_DENSE_BF16X3) return KQ_ERR_FORMAT;
+  if (nb < 0 || nb > INT32_MAX) return KQ_ERR_SHAPE;
+  if (nb == 0) return KQ_OK;
+  if (!params || !t_out) return KQ_ERR_NULL;
+  if (!aligned(params, 4) || !aligned(t_out, 4)) return KQ_ERR_ALIGN;
+  const hipError_t e = kq::launch_expand(params, nb, tfmt, t_out, stream);
+  return e == hipSuccess ? KQ_OK : fail_hip(e);
+}
+
+int kq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, const void* t,
+                int tfmt, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, int variant,
+                void* stream) {
+  return quantize_impl(x, dtype, rows, d, ldx, t, tfmt, q, ldq, s, lds, variant, nullptr, 0,
+                       false, stream);
+}
+
+int sq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                const float* mult, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                void* stream) {
+  return sq_impl(x, dtype, rows, d, ldx, mult, q, ldq, s, lds, nullptr, 0, false, stream);
+}
+
+int kq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                       const void* t, int tfmt, uint8_t* q, int64_t ldq, uint8_t* s,
+                       int64_t lds, int variant, float* y, int64_t ldy, void* stream) {
+  return quantize_impl(x, dtype, rows, d, ldx, t, tfmt, q, ldq, s, lds, variant, y, ldy, true,
+                       stream);
+}
+
+int sq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                       const float* mult, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                       float* y, int64_t ldy, void* stream) {
+  return sq_impl(x, dtype, rows, d, ldx, mult, q, ldq, s, lds, y, ldy, true, stream);
+}
+
+const char* kq_status_string(int status) {
+  switch (status) {
+    case KQ_OK: return "ok";
+    case KQ_ERR_NULL: return "null pointer";
+    case KQ_ERR_SHAPE: return "bad shape or pitch";
+    case KQ_ERR_ALIGN: return "misaligned pointer or pitch";
+    case KQ_ERR_DTYPE: return "unsupported dtype";
+    case KQ_ERR_FORMAT: return "unsupported transform format";
+    case KQ_ERR_VARIANT: return "unknown variant";
+    case KQ_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int kq_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// kq_butterfly.hip — in-register factored transform + MXFP4 encode (gfx950).
+//
+// One lane owns one (row, block) unit: the 32 channels of one block of one row.
+// The block transform T_b = F1 (x) ... (x) F5 (KroQuant researchpod summary,
+// method paragraph: Kronecker product of five 2x2 unit-determinant LU factors)
+// is applied without ever forming the 32x32 matrix.  Each factor
+//     F = L*U = [[1,0],[l,1]] * [[u,v],[0,1/u]]
+// splits further into  F = L * S * D  with  S = [[1, u*v],[0,1]]  (a shear) and
+// D = diag(u, 1/u).  By the mixed-product rule of the Kronecker product,
+//     T_b = (L1 (x) .. (x) L5) (S1 (x) .. (x) S5) (D1 (x) .. (x) D5),
+// and each of the three Kronecker products is a product of commuting one-bit
+// operators.  So the kernel
+//   1. multiplies channel i by d_i = prod_k (bit(4-k) of i ? 1/u_k : u_k)   (1 mul)
+//   2. applies the five upper shears  x_p += (u_k v_k) x_q                 (5 x 16 fma)
+//   3. applies the five lower shears  x_q += l_k x_p                       (5 x 16 fma)
+// where p < q are the index pairs that differ in bit 4-k.  That is 6 fp32
+// operations per element instead of 10 for the 2x2 butterfly and 64 for the
+// dense product, and everything stays in VGPRs.
+//
+// Lanes advance through the rows with a stride that is a multiple of nb, so
+// every lane keeps one block index for its whole life and computes its 42
+// per-block constants (32 d_i, 5 shear and 5 lower coefficients) once.
+#include "kq_device.hpp"
+#include "kq_launch.hpp"
+
+// Products and sums round separately unless written as an explicit fma.
+#pragma clang fp contract(off)
+
+namespace kq {
+namespace {
+
+struct BlockConsts {
+  float d[kBlk];
+  float su[5];  // u_k * v_k
+  float ll[5];  // l_k
+};
+
+__device__ __forceinline__ void make_consts(const float* __restrict__ params, int64_t b,
+                                            BlockConsts& c) {
+  const float* p = params + b * 15;
+  float u[5], iu[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const float l = p[3 * k + 0], uk = p[3 * k + 1], v = p[3 * k + 2];
+    u[k] = uk;
+    iu[k] = 1.0f / uk;
+    c.su[k] = uk * v;
+    c.ll[k] = l;
+  }
+  // d = [u1, 1/u1] (x) [u2, 1/u2] (x) ... (x) [u5, 1/u5], built from the right.
+  c.d[0] = u[4];
+  c.d[1] = iu[4];
+  int n = 2;
+#pragma unroll
+  for (int k = 3; k >= 0; --k) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < n) {
+        c.d[n + i] = iu[k] * c.d[i];
+        c.d[i] = u[k] * c.d[i];
+      }
+    }
+    n *= 2;
+  }
+}
+
+__device__ __forceinline__ void transform(float (&v)[kBlk], const BlockConsts& c) {
+#pragma unroll
+  for (int i = 0; i < kBlk; ++i) v[i] *= c.d[i];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int st = 16 >> k;
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i)
+      if (!(i & st)) v[i] = __builtin_fmaf(c.su[k], v[i + st], v[i]);
+  }
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int st = 16 >> k;
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i)
+      if (!(i & st)) v[i + st] = __builtin_fmaf(c.ll[k], v[i], v[i + st]);
+  }
+}
+
+template <int DT, bool WRITE_Y>
+__global__ __launch_bounds__(kThreads) void butterfly_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t nb, int64_t ldx,
+    const float* __restrict__ params, uint8_t* __restrict__ q, int64_t ldq,
+    uint8_t* __restrict__ s, int64_t lds, float* __restrict__ y, int64_t ldy) {
+  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t lanes = (int64_t)gridDim.x * kThreads;  // a multiple of nb
+  const int64_t b = gtid % nb;
+  int64_t t = gtid / nb;
+  const int64_t tstep = lanes / nb;
+  auto body = [&](const Raw<DT>& raw, int64_t r, const BlockConsts& c) {
+    float v[kBlk];
+    unpack(raw, v);
+    transform(v, c);
+    if (WRITE_Y) store_y(y + r * ldy + b * kBlk, v);
+    encode_store(v, q + r * ldq + b * (kBlk / 2), s + r * lds + b);
+  };
+#if KQ_LDS_STAGE
+  if constexpr (DT == DT_BF16) {
+    __shared__ uint4 stage[kThreads / 64][64][5];
+    if ((gtid - (threadIdx.x & 63)) / nb >= rows) return;  // whole wave past the end
+    BlockConsts c;
+    make_consts(params, b, c);
+    for_each_row_lds(x, rows, ldx, nb, gtid, lanes, stage[threadIdx.x >> 6],
+                     [&](const Raw<DT_BF16>& raw, int64_t r) { body(raw, r, c); });
+    return;
+  }
+#endif
+  if (t >= rows) return;
+  BlockConsts c;
+  make_consts(params, b, c);
+  for_each_row<DT>(x, rows, ldx, b * kBlk, t, tstep,
+                   [&](const Raw<DT>& raw, int64_t r) { body(raw, r, c); });
+}
+
+template <int DT, bool WRITE_Y>
+hipError_t launch_t(const LaunchArgs& a) {
+  const int64_t grid = grid_for_units(a.rows, a.nb, a.cus, kButterflyBlocksPerCU);
+  hipLaunchKernelGGL((butterfly_kernel<DT, WRITE_Y>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     (hipStream_t)a.stream, a.x, a.rows, a.nb, a.ldx, (const float*)a.t, a.q,
+                     a.ldq, a.s, a.lds, a.y, a.ldy);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_butterfly(const LaunchArgs& a) {
+  if (a.dtype == DT_BF16) return a.y ? launch_t<DT_BF16, true>(a) : launch_t<DT_BF16, false>(a);
+  return a.y ? launch_t<DT_FP32, true>(a) : launch_t<DT_FP32, false>(a);
+}
+
+}  // namespace kq

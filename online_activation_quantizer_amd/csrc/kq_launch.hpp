@@ -1,0 +1,58 @@
+// kq_launch.hpp — host-side launch plumbing shared by the kernel files and the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kq {
+
+constexpr int kThreads = 256;             // threads per workgroup (4 wave64)
+#ifndef KQ_BPCU
+#define KQ_BPCU 2
+#endif
+constexpr int kButterflyBlocksPerCU = KQ_BPCU;  // resident-grid target of the unit-per-lane kernels
+
+struct LaunchArgs {
+  const void* x;
+  int dtype;
+  int64_t rows, d, nb, ldx;
+  const void* t;  // params / expanded transform / SmoothQuant multipliers
+  uint8_t* q;
+  int64_t ldq;
+  uint8_t* s;
+  int64_t lds;
+  float* y;  // optional fp32 pre-quantization output (validation entry points)
+  int64_t ldy;
+  void* stream;
+  int cus;  // compute units of the current device
+};
+
+inline int64_t gcd64(int64_t a, int64_t b) {
+  while (b) {
+    const int64_t r = a % b;
+    a = b;
+    b = r;
+  }
+  return a;
+}
+
+// Grid for the unit-per-lane kernels: the lane count (grid * kThreads) must be a
+// multiple of nb so each lane keeps one block index; aim for blocks_per_cu
+// workgroups per compute unit but never more lanes than (row, block) units
+// (rounded up to the next legal size).
+inline int64_t grid_for_units(int64_t rows, int64_t nb, int cus, int blocks_per_cu) {
+  const int64_t m = nb / gcd64(nb, kThreads);  // grid granule
+  const int64_t units = rows * nb;
+  const int64_t need = (units + kThreads - 1) / kThreads;
+  int64_t target = (int64_t)cus * blocks_per_cu;
+  if (target > need) target = need;
+  int64_t k = (target + m - 1) / m;
+  if (k < 1) k = 1;
+  return k * m;
+}
+
+hipError_t launch_butterfly(const LaunchArgs& a);
+hipError_t launch_sq(const LaunchArgs& a);
+hipError_t launch_mfma(const LaunchArgs& a);
+hipError_t launch_expand(const float* params, int64_t nb, int tfmt, void* out, void* stream);
+
+}  // namespace kq

@@ -1,0 +1,65 @@
+// kq_sq.hip — SmoothQuant baseline on the same memory skeleton as the
+// butterfly kernel: per-channel multiply y_c = x_c * mult_c (mult = 1/s_c, the
+// per-channel smoothing the KroQuant abstract compares against), then the same
+// MXFP4 encode and stores.  Each lane keeps its block's 32 multipliers in VGPRs.
+#include "kq_device.hpp"
+#include "kq_launch.hpp"
+
+// Products and sums round separately unless written as an explicit fma.
+#pragma clang fp contract(off)
+
+namespace kq {
+namespace {
+
+template <int DT, bool WRITE_Y>
+__global__ __launch_bounds__(kThreads) void sq_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t nb, int64_t ldx,
+    const float* __restrict__ mult, uint8_t* __restrict__ q, int64_t ldq,
+    uint8_t* __restrict__ s, int64_t lds, float* __restrict__ y, int64_t ldy) {
+  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t lanes = (int64_t)gridDim.x * kThreads;
+  const int64_t b = gtid % nb;
+  int64_t t = gtid / nb;
+  const int64_t tstep = lanes / nb;
+  if (t >= rows) return;
+
+  float m[kBlk];
+  {
+    const float4* mp = reinterpret_cast<const float4*>(mult + b * kBlk);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 f = mp[k];
+      m[4 * k] = f.x;
+      m[4 * k + 1] = f.y;
+      m[4 * k + 2] = f.z;
+      m[4 * k + 3] = f.w;
+    }
+  }
+
+  for_each_row<DT>(x, rows, ldx, b * kBlk, t, tstep, [&](const Raw<DT>& raw, int64_t r) {
+    float v[kBlk];
+    unpack(raw, v);
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i) v[i] *= m[i];
+    if (WRITE_Y) store_y(y + r * ldy + b * kBlk, v);
+    encode_store(v, q + r * ldq + b * (kBlk / 2), s + r * lds + b);
+  });
+}
+
+template <int DT, bool WRITE_Y>
+hipError_t launch_t(const LaunchArgs& a) {
+  const int64_t grid = grid_for_units(a.rows, a.nb, a.cus, kButterflyBlocksPerCU);
+  hipLaunchKernelGGL((sq_kernel<DT, WRITE_Y>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     (hipStream_t)a.stream, a.x, a.rows, a.nb, a.ldx, (const float*)a.t, a.q,
+                     a.ldq, a.s, a.lds, a.y, a.ldy);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sq(const LaunchArgs& a) {
+  if (a.dtype == DT_BF16) return a.y ? launch_t<DT_BF16, true>(a) : launch_t<DT_BF16, false>(a);
+  return a.y ? launch_t<DT_FP32, true>(a) : launch_t<DT_FP32, false>(a);
+}
+
+}  // namespace kq

@@ -75,3 +75,22 @@ def make_inputs(cfg: Config, rows: int | None = None, seed: int | None = None):
     params = make_params(cfg.nb, rng)
     mult = make_sq_mult(cfg.d, rng)
     return x, params, mult
+
+
+def make_activations_device(cfg: Config, seed: int, device="cuda"):
+    """Same value model drawn on the GPU with torch's seeded generator (for the
+    multi-gigabyte batched sweep, where host generation would dominate).  Returns a
+    torch tensor: bfloat16 (cfg.dtype == "bf16") or float32."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    rows, d = cfg.rows, cfg.d
+    if cfg.dist == "gauss_mean":
+        m = torch.randn((rows, 1), generator=g, device=device) * cfg.mean_std
+        x = torch.randn((rows, d), generator=g, device=device)
+        x += m
+    else:
+        raise ValueError("device generation supports the gaussian-mean model only")
+    out_ch = torch.randperm(d, generator=g, device=device)[: cfg.n_outliers]
+    x[:, out_ch] *= cfg.outlier_scale
+    return x.to(torch.bfloat16) if cfg.dtype == "bf16" else x

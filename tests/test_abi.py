@@ -1,0 +1,111 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import online_activation_quantizer_amd as kq
+    from online_activation_quantizer_amd import build
+    if not os.path.exists(build.LIB_PATH):
+        build.build()
+    return kq.lib()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "kq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported(L):
+    names = header_functions()
+    assert {"kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
+            "sq_transform_debug", "kq_status_string", "kq_last_hip_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_oracle_not_linked_into_product(L):
+    # the product library must not contain the oracle's entry points
+    for n in ("oq_quantize", "oq_encode", "oq_classify"):
+        assert not hasattr(L, n)
+
+
+# fake, suitably aligned device addresses: validation never dereferences them
+X, T, Q, S, Y = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+OK, NULL, SHAPE, ALIGN, DTYPE, FORMAT, VARIANT = 0, -1, -2, -3, -4, -5, -6
+
+
+def quant(L, x=X, dtype=0, rows=4, d=64, ldx=64, t=T, tfmt=0, q=Q, ldq=32, s=S, lds=2, variant=0):
+    return L.kq_quantize(x, dtype, rows, d, ldx, t, tfmt, q, ldq, s, lds, variant, None)
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(dtype=7), DTYPE),
+    (dict(d=48, ldx=48), SHAPE),
+    (dict(d=0, ldx=0), SHAPE),
+    (dict(rows=-1), SHAPE),
+    (dict(ldx=32), SHAPE),
+    (dict(ldq=16), SHAPE),
+    (dict(lds=1), SHAPE),
+    (dict(x=None), NULL),
+    (dict(t=None), NULL),
+    (dict(q=None), NULL),
+    (dict(s=None), NULL),
+    (dict(x=X + 8), ALIGN),
+    (dict(q=Q + 4), ALIGN),
+    (dict(ldx=68), ALIGN),
+    (dict(ldq=40), ALIGN),
+    (dict(t=T + 2), ALIGN),
+    (dict(tfmt=9), FORMAT),
+    (dict(tfmt=1), FORMAT),          # dense fp32 is not a kq_quantize input
+    (dict(tfmt=0, variant=2), FORMAT),  # matrix cores need the bf16x3 split
+    (dict(tfmt=2, variant=1), FORMAT),  # the butterfly needs the factors
+    (dict(variant=5), VARIANT),
+    (dict(tfmt=2, variant=2, dtype=1), DTYPE),  # matrix-core path takes bf16 only
+    (dict(rows=0, x=None, t=None, q=None, s=None), OK),  # no-op, no HIP call
+])
+def test_quantize_validation(L, kw, rc):
+    assert quant(L, **kw) == rc
+
+
+def test_sq_and_debug_validation(L):
+    assert L.sq_quantize(X, 0, 4, 64, 64, None, Q, 32, S, 2, None) == NULL
+    assert L.sq_quantize(X, 0, 4, 64, 64, T + 4, Q, 32, S, 2, None) == ALIGN  # mult needs 16 B
+    assert L.sq_quantize(X, 3, 4, 64, 64, T, Q, 32, S, 2, None) == DTYPE
+    assert L.sq_quantize(None, 0, 0, 64, 64, None, None, 32, None, 2, None) == OK
+    assert L.kq_transform_debug(X, 0, 4, 64, 64, T, 0, Q, 32, S, 2, 0, None, 64, None) == NULL
+    assert L.kq_transform_debug(X, 0, 4, 64, 64, T, 0, Q, 32, S, 2, 0, Y, 32, None) == SHAPE
+    assert L.kq_transform_debug(X, 0, 4, 64, 64, T, 0, Q, 32, S, 2, 0, Y + 2, 64, None) == ALIGN
+    assert L.sq_transform_debug(X, 0, 4, 64, 64, T, Q, 32, S, 2, None, 64, None) == NULL
+
+
+def test_expand_validation(L):
+    assert L.kq_expand_factors(T, 4, 0, Y, None) == FORMAT  # params need no expansion
+    assert L.kq_expand_factors(T, 4, 7, Y, None) == FORMAT
+    assert L.kq_expand_factors(T, -1, 1, Y, None) == SHAPE
+    assert L.kq_expand_factors(None, 4, 1, Y, None) == NULL
+    assert L.kq_expand_factors(T, 4, 1, None, None) == NULL
+    assert L.kq_expand_factors(T + 1, 4, 1, Y, None) == ALIGN
+    assert L.kq_expand_factors(None, 0, 2, None, None) == OK
+
+
+def test_status_strings(L):
+    for st in range(-7, 1):
+        assert L.kq_status_string(st)
+    assert L.kq_status_string(-100) == b"unknown status"
+    assert L.kq_last_hip_error() == 0
+
+
+def test_binding_rejects_unknown_dtype():
+    torch = pytest.importorskip("torch")
+    import online_activation_quantizer_amd as kq
+    with pytest.raises(kq.KQError):
+        kq.kq_quantize(torch.zeros((2, 32), dtype=torch.float64), torch.zeros(15))

@@ -1,0 +1,204 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Rule (fp32 transform): pre-quantization values within 1e-5 * max|x_block| of the
+oracle everywhere; E8M0 scales and E2M1 codes bit-exact except where the
+oracle's value lies within that tolerance of a decision boundary (counted, and
+below 1e-4 of elements); nothing else may differ.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import online_activation_quantizer_amd as kq
+from gpu_util import dev, host, run_kq, say, verdict
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = ["tiny", "pixart", "sana", "flux", "flux_mlp"]
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_kq_parity_full_config(name):
+    cfg = synth.get_config(name)
+    say(f"[kq parity] {name} {cfg.rows}x{cfg.d} {cfg.dtype}")
+    x, p, _ = synth.make_inputs(cfg)
+    q, s, y = run_kq(x, p)
+    _, _, y_o = oracle.quantize(x, p, want_y=True)
+    st = verdict(x, y_o, q, s, y_c=y)
+    say(f"  {st}")
+    assert st["pass"], st
+
+
+@pytest.mark.parametrize("name", ["pixart", "flux"])
+def test_sq_parity(name):
+    cfg = synth.get_config(name)
+    say(f"[sq parity] {name}")
+    x, _, m = synth.make_inputs(cfg)
+    xd, md = dev(x), dev(m)
+    q, s = kq.sq_quantize(xd, md)
+    q2, s2, yd = kq.sq_transform_debug(xd, md)
+    import torch
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(s, s2)
+    _, _, y_o = oracle.sq_quantize(x, m, want_y=True)
+    st = verdict(x, y_o, host(q), host(s), y_c=host(yd))
+    say(f"  {st}")
+    assert st["pass"], st
+
+
+def test_identity_factors_are_plain_mxfp4_exactly():
+    cfg = synth.get_config("pixart")
+    say("[identity] pixart")
+    x, _, _ = synth.make_inputs(cfg)
+    p = synth.make_identity_params(cfg.nb)
+    q, s, y = run_kq(x, p)
+    q_o, s_o = oracle.encode(synth.f32_from_bf16_bits(x).astype(np.float64))
+    assert np.array_equal(y, synth.f32_from_bf16_bits(x))
+    assert np.array_equal(s, s_o)
+    assert np.array_equal(q, q_o)
+
+
+def test_encoder_black_box_every_fp32_in_range():
+    """Every fp32 magnitude in [2^-3, 8) (both signs) through the product path with
+    identity factors at scale 2^0, against the oracle's element encoder: exact."""
+    say("[encoder sweep] fp32 [0.125, 8)")
+    lo, hi = np.float32(0.125).view(np.uint32), np.float32(8.0).view(np.uint32)
+    vals = np.arange(lo, hi, dtype=np.uint32).view(np.float32)
+    vals = vals * np.where(np.arange(vals.size) % 2 == 0, 1, -1).astype(np.float32)
+    per = 31
+    nblk = -(-vals.size // per)
+    blocks = np.zeros((nblk, 32), np.float32)
+    blocks[:, 0] = 7.99  # anchors every block's amax in [7.99, 8): scale 2^0
+    flat = blocks[:, 1:].reshape(-1)
+    flat[: vals.size] = vals
+    blocks[:, 1:] = flat.reshape(nblk, per)
+    d = 2048
+    rows = -(-nblk // (d // 32))
+    x = np.zeros((rows * (d // 32), 32), np.float32)
+    x[:nblk] = blocks
+    x[nblk:, 0] = 7.99
+    x = x.reshape(rows, d)
+    q, s, _ = run_kq(x, synth.make_identity_params(d // 32), debug=False)
+    q_o, s_o = oracle.encode(x.astype(np.float64))
+    assert np.all(s_o == 127)
+    assert np.array_equal(s, s_o)
+    bad = np.count_nonzero(q != q_o)
+    assert bad == 0, f"{bad} code bytes differ"
+
+
+@pytest.mark.parametrize("k", [-149, -140, -127, -126, -110, -100, -30, 0, 30, 100, 115, 125])
+def test_extreme_scales(k):
+    """Blocks scaled by 2^k (fp32 input): scale bytes from 0 to 252.  Identity factors
+    (no rounding in the transform) must match exactly at every k, subnormal inputs
+    included.  Random factors run where fp32 arithmetic keeps its relative precision
+    (|x| above the subnormal range, so the 1e-5 * max|x| rule is attainable) and
+    below 2^116 (so |T_b x| < 2^128)."""
+    say(f"[extreme scale] 2^{k}")
+    rng = np.random.default_rng(1000 + k)
+    x = (rng.normal(size=(64, 256)) * 2.0 ** k).astype(np.float32)
+    p = synth.make_identity_params(8)
+    q, s, y = run_kq(x, p)
+    q_o, s_o = oracle.encode(x.astype(np.float64))
+    assert np.array_equal(y, x)
+    assert np.array_equal(s, s_o) and np.array_equal(q, q_o)
+    if -120 <= k <= 115:
+        p = synth.make_params(8, rng)
+        q, s, y = run_kq(x, p)
+        _, _, y_o = oracle.quantize(x, p, want_y=True)
+        st = verdict(x, y_o, q, s, y_c=y)
+        assert st["pass"], st
+
+
+def test_zero_nan_inf_blocks():
+    say("[special blocks]")
+    x = np.ones((4, 128), np.float32)
+    x[0, :32] = 0.0
+    x[1, 40] = np.nan
+    x[2, 70] = np.inf
+    x[3, 100] = -np.inf
+    p = synth.make_identity_params(4)
+    q, s, _ = run_kq(x, p, debug=False)
+    q_o, s_o = oracle.encode(x.astype(np.float64))
+    assert s[0, 0] == 0 and not q[0, :16].any()
+    assert s[1, 1] == 0xFF and s[2, 2] == 0xFF and s[3, 3] == 0xFF
+    assert np.array_equal(s, s_o) and np.array_equal(q, q_o)
+
+
+@pytest.mark.parametrize("rows", [1, 2, 31, 33, 257])
+@pytest.mark.parametrize("d", [32, 96, 3104])
+def test_ragged_shapes_match_oracle(rows, d):
+    """Row counts around tile edges and block counts of 1, 3 and 97 (prime) blocks."""
+    say(f"[ragged] rows={rows} d={d}")
+    rng = np.random.default_rng(rows * 7919 + d)
+    x = synth.bf16_bits_from_f32(rng.standard_t(3, size=(rows, d)).astype(np.float32) * 3)
+    p = synth.make_params(d // 32, rng)
+    q, s, y = run_kq(x, p)
+    _, _, y_o = oracle.quantize(x, p, want_y=True)
+    st = verdict(x, y_o, q, s, y_c=y)
+    assert st["pass"], st
+
+
+def test_row_subsets_and_pitches_with_canaries():
+    import torch
+    cfg = synth.get_config("sana")
+    say("[pitch] sana rows 300, padded x/q/s pitches, canaries")
+    x, p, _ = synth.make_inputs(cfg, rows=300)
+    q_full, s_full, _ = run_kq(x, p, debug=False)
+    d = cfg.d
+    xw = np.zeros((300, d + 64), np.uint16)
+    xw[:, :d] = x
+    xw[:, d:] = synth.bf16_bits_from_f32(np.full((300, 64), 3e38, np.float32))  # never read
+    xd = dev(xw)[:, :d]
+    pd = dev(p)
+    qbuf = torch.full((300, d // 2 + 48), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((300, d // 32 + 9), 0x5A, dtype=torch.uint8, device="cuda")
+    kq.kq_quantize(xd, pd, kq.KQ_T_PARAMS, kq.KQ_AUTO, q=qbuf[:, : d // 2], s=sbuf[:, : d // 32])
+    qb, sb = host(qbuf), host(sbuf)
+    assert np.array_equal(qb[:, : d // 2], q_full) and np.array_equal(sb[:, : d // 32], s_full)
+    assert np.all(qb[:, d // 2:] == 0xA5) and np.all(sb[:, d // 32:] == 0x5A)
+    for r0, r1 in [(0, 1), (5, 36), (299, 300)]:
+        qs, ss, _ = run_kq(np.ascontiguousarray(x[r0:r1]), p, debug=False)
+        assert np.array_equal(qs, q_full[r0:r1]) and np.array_equal(ss, s_full[r0:r1])
+
+
+def test_deterministic_and_side_stream():
+    import torch
+    cfg = synth.get_config("pixart")
+    say("[determinism] pixart, side stream")
+    x, p, _ = synth.make_inputs(cfg, rows=1024)
+    xd, pd = dev(x), dev(p)
+    q1, s1 = kq.kq_quantize(xd, pd)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        q2, s2 = kq.kq_quantize(xd, pd, stream=st)
+    st.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+
+
+def test_expand_dense_f32_and_bf16x3():
+    import torch
+    say("[expand] 384 blocks")
+    p = synth.make_params(384, np.random.default_rng(55))
+    pd = dev(p)
+    Tf = host(kq.kq_expand_factors(pd, kq.KQ_T_DENSE_F32)).reshape(384, 32, 32).astype(np.float64)
+    T_o = oracle.expand(p)
+    # error bound of the fp32 evaluation: each factor entry carries at most 3 roundings
+    # (l*v, 1/u, their sum) and the product of five entries 4 more, so
+    # |T_gpu - T| <= 16 eps * kron_k(|F_k| with |l v| + |1/u| in the (1,1) slot)
+    bound = np.ones((384, 1, 1))
+    for k in range(5):
+        l, u, v = (p[:, k, i].astype(np.float64) for i in range(3))
+        A = np.stack([np.stack([np.abs(u), np.abs(v)], -1),
+                      np.stack([np.abs(l * u), np.abs(l * v) + np.abs(1 / u)], -1)], -2)
+        bound = np.einsum("bij,bkl->bikjl", bound, A).reshape(384, bound.shape[1] * 2, -1)
+    assert np.all(np.abs(Tf - T_o) <= 16 * 2.0 ** -24 * bound)
+    T3 = kq.kq_expand_factors(pd, kq.KQ_T_DENSE_BF16X3)
+    parts = host(T3).reshape(3, 384, 32, 32).astype(np.uint32) << 16
+    hi, mid, lo = (parts[i].view(np.float32).astype(np.float64) for i in range(3))
+    # the three bf16 parts sum exactly to the fp32 dense entry
+    assert np.array_equal(hi + mid + lo, Tf)
+    assert np.all(np.abs(mid) <= np.abs(hi) * 2.0 ** -8) and np.all(np.abs(lo) <= np.abs(mid) * 2.0 ** -8 + 0)
+    torch.cuda.synchronize()

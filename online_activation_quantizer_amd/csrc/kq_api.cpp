@@ -42,6 +42,9 @@ int current_cus(int* cus) {
   return KQ_OK;
 }
 
+// Kernels index lanes with 32-bit arithmetic: at most 2^22 blocks (d <= 2^27).
+constexpr int64_t kMaxBlocks = int64_t(1) << 22;
+
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int elem_size(int dtype) { return dtype == KQ_BF16 ? 2 : 4; }
@@ -52,7 +55,7 @@ int check_common(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
   if (dtype != KQ_BF16 && dtype != KQ_FP32) return KQ_ERR_DTYPE;
   if (rows < 0 || d <= 0 || d % 32 != 0 || ldx < d || ldq < d / 2 || lds < d / 32)
     return KQ_ERR_SHAPE;
-  if (d / 32 > INT32_MAX) return KQ_ERR_SHAPE;
+  if (d / 32 > kMaxBlocks) return KQ_ERR_SHAPE;
   if (rows == 0) return KQ_OK;
   if (!x || !t || !q || !s) return KQ_ERR_NULL;
   if (!aligned(x, 16) || (ldx * elem_size(dtype)) % 16 != 0 || !aligned(q, 16) || ldq % 16 != 0)

@@ -17,9 +17,11 @@
 // operations per element instead of 10 for the 2x2 butterfly and 64 for the
 // dense product, and everything stays in VGPRs.
 //
-// Lanes advance through the rows with a stride that is a multiple of nb, so
-// every lane keeps one block index for its whole life and computes its 42
-// per-block constants (32 d_i, 5 shear and 5 lower coefficients) once.
+// Lanes cover consecutive (row, block) units in memory order (a wave reads 4 KB
+// contiguous per row step) and advance through the rows with a stride that is a
+// multiple of nb, so every lane keeps one block for its whole life and computes
+// its 42 constants (32 d_i, 5 upper and 5 lower shear coefficients) once, while
+// its first row is already in flight.
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
@@ -35,9 +37,10 @@ struct BlockConsts {
   float ll[5];  // l_k
 };
 
-__device__ __forceinline__ void make_consts(const float* __restrict__ params, int64_t b,
+// The 42 constants of block b, computed by the lane that owns it.
+__device__ __forceinline__ void make_consts(const float* __restrict__ params, uint32_t b,
                                             BlockConsts& c) {
-  const float* p = params + b * 15;
+  const float* p = params + (size_t)b * 15;
   float u[5], iu[5];
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
@@ -50,9 +53,8 @@ __device__ __forceinline__ void make_consts(const float* __restrict__ params, in
   // d = [u1, 1/u1] (x) [u2, 1/u2] (x) ... (x) [u5, 1/u5], built from the right.
   c.d[0] = u[4];
   c.d[1] = iu[4];
-  int n = 2;
 #pragma unroll
-  for (int k = 3; k >= 0; --k) {
+  for (int k = 3, n = 2; k >= 0; --k, n *= 2) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i < n) {
@@ -60,7 +62,6 @@ __device__ __forceinline__ void make_consts(const float* __restrict__ params, in
         c.d[i] = u[k] * c.d[i];
       }
     }
-    n *= 2;
   }
 }
 
@@ -85,45 +86,32 @@ __device__ __forceinline__ void transform(float (&v)[kBlk], const BlockConsts& c
 
 template <int DT, bool WRITE_Y>
 __global__ __launch_bounds__(kThreads) void butterfly_kernel(
-    const void* __restrict__ x, int64_t rows, int64_t nb, int64_t ldx,
+    const void* __restrict__ x, int64_t rows, uint32_t nb, int64_t ldx, uint32_t tstep,
     const float* __restrict__ params, uint8_t* __restrict__ q, int64_t ldq,
     uint8_t* __restrict__ s, int64_t lds, float* __restrict__ y, int64_t ldy) {
-  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t lanes = (int64_t)gridDim.x * kThreads;  // a multiple of nb
-  const int64_t b = gtid % nb;
-  int64_t t = gtid / nb;
-  const int64_t tstep = lanes / nb;
-  auto body = [&](const Raw<DT>& raw, int64_t r, const BlockConsts& c) {
-    float v[kBlk];
-    unpack(raw, v);
+  // the lane count gridDim.x * kThreads is a multiple of nb (tstep rows per pass)
+  const uint32_t gtid = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t b = gtid % nb;
+  const int64_t t = gtid / nb;
+  if (t >= rows) return;
+  // first row in flight before the per-block set-up
+  const Raw<DT> first = load_raw<DT>(x, t * ldx + b * kBlk);
+  BlockConsts c;
+  make_consts(params, b, c);
+  for_each_row<DT>(x, rows, ldx, b * kBlk, t, tstep, first, [&](float (&v)[kBlk], int64_t r) {
     transform(v, c);
     if (WRITE_Y) store_y(y + r * ldy + b * kBlk, v);
     encode_store(v, q + r * ldq + b * (kBlk / 2), s + r * lds + b);
-  };
-#if KQ_LDS_STAGE
-  if constexpr (DT == DT_BF16) {
-    __shared__ uint4 stage[kThreads / 64][64][5];
-    if ((gtid - (threadIdx.x & 63)) / nb >= rows) return;  // whole wave past the end
-    BlockConsts c;
-    make_consts(params, b, c);
-    for_each_row_lds(x, rows, ldx, nb, gtid, lanes, stage[threadIdx.x >> 6],
-                     [&](const Raw<DT_BF16>& raw, int64_t r) { body(raw, r, c); });
-    return;
-  }
-#endif
-  if (t >= rows) return;
-  BlockConsts c;
-  make_consts(params, b, c);
-  for_each_row<DT>(x, rows, ldx, b * kBlk, t, tstep,
-                   [&](const Raw<DT>& raw, int64_t r) { body(raw, r, c); });
+  });
 }
 
 template <int DT, bool WRITE_Y>
 hipError_t launch_t(const LaunchArgs& a) {
-  const int64_t grid = grid_for_units(a.rows, a.nb, a.cus, kButterflyBlocksPerCU);
+  uint32_t tstep = 0;
+  const int64_t grid = grid_for_units(a.rows, a.nb, a.cus, kBlocksPerCU, &tstep);
   hipLaunchKernelGGL((butterfly_kernel<DT, WRITE_Y>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     (hipStream_t)a.stream, a.x, a.rows, a.nb, a.ldx, (const float*)a.t, a.q,
-                     a.ldq, a.s, a.lds, a.y, a.ldy);
+                     (hipStream_t)a.stream, a.x, a.rows, (uint32_t)a.nb, a.ldx, tstep,
+                     (const float*)a.t, a.q, a.ldq, a.s, a.lds, a.y, a.ldy);
   return hipGetLastError();
 }
 

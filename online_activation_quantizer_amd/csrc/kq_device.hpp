@@ -5,10 +5,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#ifndef KQ_NT_LOAD
-#define KQ_NT_LOAD 0
-#endif
-
 namespace kq {
 
 constexpr int kBlk = 32;  // channels per transform block and per MX block
@@ -26,91 +22,8 @@ __device__ __forceinline__ Raw<DT> load_raw(const void* x, int64_t elem_off) {
   const uint4* p = reinterpret_cast<const uint4*>(
       static_cast<const char*>(x) + elem_off * (DT == DT_BF16 ? 2 : 4));
 #pragma unroll
-  for (int k = 0; k < (int)(sizeof(r.w) / sizeof(uint4)); ++k) {
-#if KQ_NT_LOAD
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + k));
-    r.w[k] = make_uint4(v.x, v.y, v.z, v.w);
-#else
-    r.w[k] = p[k];
-#endif
-  }
+  for (int k = 0; k < (int)(sizeof(r.w) / sizeof(uint4)); ++k) r.w[k] = p[k];
   return r;
-}
-
-// Walk rows t, t + tstep, ... < rows of one lane's block column `col` (element
-// offset), calling f(raw, row) for each.  Two-stage software pipeline: the next
-// row's load is issued before the current row is processed.  The prefetch is
-// unconditional (its row is clamped to the last row, an in-bounds re-read) so
-// the compiler can keep exact counts of the loads in flight.
-template <int DT, class F>
-__device__ __forceinline__ void for_each_row(const void* __restrict__ x, int64_t rows, int64_t ldx,
-                                             int64_t col, int64_t t, int64_t tstep, F&& f) {
-  const int64_t last = rows - 1;
-  Raw<DT> ra = load_raw<DT>(x, t * ldx + col);
-  for (;;) {
-    int64_t tn = t + tstep;
-    Raw<DT> rb = load_raw<DT>(x, (tn < last ? tn : last) * ldx + col);
-    f(ra, t);
-    if (tn > last) return;
-    t = tn;
-    tn = t + tstep;
-    ra = load_raw<DT>(x, (tn < last ? tn : last) * ldx + col);
-    f(rb, t);
-    if (tn > last) return;
-    t = tn;
-  }
-}
-
-#ifndef KQ_LDS_STAGE
-#define KQ_LDS_STAGE 0
-#endif
-
-// LDS-staged walker for bf16 input (one wave = 64 consecutive units).  The wave
-// loads its 4 KB with fully coalesced 16-byte lanes (lane l fetches chunk l%4 of
-// unit 16k + l/4), parks the chunks in LDS (80-byte unit pitch: conflict-free
-// reads) and each lane then reads back its own unit.  g is the lane's flat unit
-// index; G (the grid's lane count) is a multiple of nb.  Every lane of the wave
-// stays in the loop while the wave's first unit is in range.
-template <class F>
-__device__ __forceinline__ void for_each_row_lds(const void* __restrict__ x, int64_t rows,
-                                                 int64_t ldx, int64_t nb, int64_t g, int64_t G,
-                                                 uint4 (*__restrict__ wlds)[5], F&& f) {
-  const int lane = threadIdx.x & 63;
-  const int64_t u0 = g - lane;
-  const int64_t tstep = G / nb;
-  const int64_t last = rows - 1;
-  int64_t rk[4], ck[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t uk = u0 + 16 * k + (lane >> 2);
-    rk[k] = uk / nb;
-    ck[k] = (uk % nb) * kBlk + (lane & 3) * 8;
-  }
-  const uint16_t* xb = static_cast<const uint16_t*>(x);
-  int64_t t = g / nb;
-  int64_t t0 = u0 / nb;
-  for (; t0 <= last; t0 += tstep, t += tstep) {
-    uint4 c[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t r = rk[k] < last ? rk[k] : last;
-      c[k] = *reinterpret_cast<const uint4*>(xb + r * ldx + ck[k]);
-      rk[k] += tstep;
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) wlds[16 * k + (lane >> 2)][lane & 3] = c[k];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    Raw<DT_BF16> mine;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) mine.w[k] = wlds[lane][k];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (t <= last) f(mine, t);
-  }
 }
 
 // Widen to fp32.  bf16 is the top half of an fp32, so the widening is exact.
@@ -133,6 +46,41 @@ __device__ __forceinline__ void unpack(const Raw<DT_FP32>& r, float (&v)[kBlk]) 
     v[4 * k + 2] = __uint_as_float(r.w[k].z);
     v[4 * k + 3] = __uint_as_float(r.w[k].w);
   }
+}
+
+// Row walker.  Lane-to-unit mapping is row-major: the grid's lanes cover
+// consecutive (row, block) units, and since the lane count is a multiple of nb
+// each lane keeps one block column `col` (element offset) and walks rows t,
+// t + tstep, ... < rows, calling f(v, row) with the row's 32 values widened to
+// fp32.  `ra` holds row t, already loaded by the caller so that its latency
+// overlaps the caller's set-up work.  The loop is rotated so that the next row's
+// load is issued right after the current data is unpacked and stays in flight
+// during the whole transform, encode and store.  The prefetch is unconditional
+// (its row clamped to the last row, an in-bounds re-read), so no branch sits
+// around a memory operation and the compiler keeps exact counts of those in
+// flight.
+template <int DT, class F>
+__device__ __forceinline__ void for_each_row(const void* __restrict__ x, int64_t rows, int64_t ldx,
+                                             int64_t col, int64_t t, int64_t tstep, Raw<DT> ra,
+                                             F&& f) {
+  const int64_t last = rows - 1;
+  float v[kBlk];
+  unpack(ra, v);
+  int64_t tn = t + tstep;
+  ra = load_raw<DT>(x, (tn < last ? tn : last) * ldx + col);
+  for (;;) {
+    f(v, t);
+    if (tn > last) return;
+    t = tn;
+    tn = t + tstep;
+    unpack(ra, v);
+    ra = load_raw<DT>(x, (tn < last ? tn : last) * ldx + col);
+  }
+}
+
+// A wave-uniform value kept in a scalar register.
+__device__ __forceinline__ float uniform(float v) {
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
 }
 
 // NaN-propagating max of |a|, |b|, |c| (v_maximum3_f32 with abs modifiers).

@@ -7,9 +7,9 @@ namespace kq {
 
 constexpr int kThreads = 256;             // threads per workgroup (4 wave64)
 #ifndef KQ_BPCU
-#define KQ_BPCU 2
+#define KQ_BPCU 3
 #endif
-constexpr int kButterflyBlocksPerCU = KQ_BPCU;  // resident-grid target of the unit-per-lane kernels
+constexpr int kBlocksPerCU = KQ_BPCU;  // resident-grid target of the unit-per-lane kernels
 
 struct LaunchArgs {
   const void* x;
@@ -36,17 +36,18 @@ inline int64_t gcd64(int64_t a, int64_t b) {
 }
 
 // Grid for the unit-per-lane kernels: the lane count (grid * kThreads) must be a
-// multiple of nb so each lane keeps one block index; aim for blocks_per_cu
-// workgroups per compute unit but never more lanes than (row, block) units
-// (rounded up to the next legal size).
-inline int64_t grid_for_units(int64_t rows, int64_t nb, int cus, int blocks_per_cu) {
+// multiple of nb so each lane keeps one block; aim for blocks_per_cu workgroups
+// per compute unit but never more lanes than (row, block) units (rounded up to
+// the next legal size).  *tstep receives the row stride of every lane.
+inline int64_t grid_for_units(int64_t rows, int64_t nb, int cus, int blocks_per_cu,
+                              uint32_t* tstep) {
   const int64_t m = nb / gcd64(nb, kThreads);  // grid granule
-  const int64_t units = rows * nb;
-  const int64_t need = (units + kThreads - 1) / kThreads;
+  const int64_t need = (rows * nb + kThreads - 1) / kThreads;
   int64_t target = (int64_t)cus * blocks_per_cu;
   if (target > need) target = need;
   int64_t k = (target + m - 1) / m;
   if (k < 1) k = 1;
+  *tstep = (uint32_t)(k * m * kThreads / nb);
   return k * m;
 }
 

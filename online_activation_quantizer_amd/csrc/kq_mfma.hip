@@ -83,19 +83,18 @@ template <bool WRITE_Y>
 __global__ __launch_bounds__(kThreads) void mfma_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t nb, int64_t ldx,
     const uint16_t* __restrict__ T3, uint8_t* __restrict__ q, int64_t ldq,
-    uint8_t* __restrict__ s, int64_t lds, float* __restrict__ y, int64_t ldy) {
+    uint8_t* __restrict__ s, int64_t lds, float* __restrict__ y, int64_t ldy, uint32_t tstep) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, h = lane >> 5;
-  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);  // a multiple of npair
-  const int64_t npair = (nb + 1) / 2;
-  const int64_t pair = wave % npair;
+  // the wave count gridDim.x * 4 is a multiple of npair (tstep tiles per pass)
+  const uint32_t wave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const uint32_t npair = (uint32_t)((nb + 1) / 2);
+  const uint32_t pair = wave % npair;
   const int64_t ntiles = (rows + 31) / 32;
-  const int64_t tstep = nwaves / npair;
   int64_t tile = wave / npair;
   if (tile >= ntiles) return;
 
-  const int64_t b0 = 2 * pair;
+  const int64_t b0 = 2 * (int64_t)pair;
   const bool has2 = b0 + 1 < nb;
   int64_t bb[2] = {b0, has2 ? b0 + 1 : b0};
 
@@ -145,9 +144,10 @@ hipError_t launch_t(const LaunchArgs& a) {
   if (target > need) target = need;
   int64_t k = (target + m - 1) / m;
   if (k < 1) k = 1;
+  const uint32_t tstep = (uint32_t)(k * m * waves_per_wg / npair);
   hipLaunchKernelGGL((mfma_kernel<WRITE_Y>), dim3((unsigned)(k * m)), dim3(kThreads), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.x, a.rows, a.nb, a.ldx,
-                     (const uint16_t*)a.t, a.q, a.ldq, a.s, a.lds, a.y, a.ldy);
+                     (const uint16_t*)a.t, a.q, a.ldq, a.s, a.lds, a.y, a.ldy, tstep);
   return hipGetLastError();
 }
 

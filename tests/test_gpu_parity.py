@@ -97,10 +97,13 @@ def test_extreme_scales(k):
     say(f"[extreme scale] 2^{k}")
     rng = np.random.default_rng(1000 + k)
     x = (rng.normal(size=(64, 256)) * 2.0 ** k).astype(np.float32)
+    # draws that underflow to -0.0 become +0.0: the transform's sums give +0 for
+    # an exact zero, so -0.0 inputs sit outside the exact identity reduction
+    x[x == 0] = 0.0
     p = synth.make_identity_params(8)
     q, s, y = run_kq(x, p)
-    q_o, s_o = oracle.encode(x.astype(np.float64))
-    assert np.array_equal(y, x)
+    q_o, s_o, _ = oracle.quantize(x, p)
+    assert np.array_equal(y.view(np.uint32), x.view(np.uint32))
     assert np.array_equal(s, s_o) and np.array_equal(q, q_o)
     if -120 <= k <= 115:
         p = synth.make_params(8, rng)

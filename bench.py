@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-sq", action="store_true", help="skip the SmoothQuant baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (4 times) as the "
+                         "known-size reference for hardware byte counters")
     return ap.parse_args()
 
 
@@ -55,6 +58,32 @@ def timed(fn, steps, warmup, stream):
     end.synchronize()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+KERNEL_SOURCES = ("kq_butterfly.hip", "kq_device.hpp", "kq_launch.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kq_butterfly_flux_4608x3072_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "online_activation_quantizer_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter runs, or None when the kernel
+    sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(x, p, seconds):
@@ -154,7 +183,8 @@ def main():
                                f"{nb} factor sets, {args.variant}",
                    "rows": rows, "d": d, "input": "bf16", "pool_sets": P},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic() if args.variant == "butterfly" else None},
         "hbm_pct": round(100 * gbs / PEAK_HBM_GBS, 2),
         "parity": parity,
     }
@@ -164,6 +194,13 @@ def main():
                               "t_sq_over_t_kq": round(sq_ms / ms, 4)}
         out["context"] = ("pages: on an MI350 the KroQuant quantizer kernel ran up to 14% faster "
                           "than a SmoothQuant kernel (shapes and timing method unstated)")
+    if args.calib_copy_mib > 0:
+        src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x0, p0, args.cpu_seconds)
     print(json.dumps(out), flush=True)

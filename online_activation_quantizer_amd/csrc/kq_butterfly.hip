@@ -37,14 +37,25 @@ struct BlockConsts {
   float ll[5];  // l_k
 };
 
-// The 42 constants of block b, computed by the lane that owns it.
-__device__ __forceinline__ void make_consts(const float* __restrict__ params, uint32_t b,
-                                            BlockConsts& c) {
-  const float* p = params + (size_t)b * 15;
+// The 15 factor parameters (l, u, v) x 5 of block b.
+struct BlockParams {
+  float p[15];
+};
+
+__device__ __forceinline__ BlockParams load_params(const float* __restrict__ params, uint32_t b) {
+  BlockParams r;
+  const float* src = params + (size_t)b * 15;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) r.p[i] = src[i];
+  return r;
+}
+
+// The 42 constants of a block from its parameters.
+__device__ __forceinline__ void make_consts(const BlockParams& bp, BlockConsts& c) {
   float u[5], iu[5];
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
-    const float l = p[3 * k + 0], uk = p[3 * k + 1], v = p[3 * k + 2];
+    const float l = bp.p[3 * k + 0], uk = bp.p[3 * k + 1], v = bp.p[3 * k + 2];
     u[k] = uk;
     iu[k] = 1.0f / uk;
     c.su[k] = uk * v;
@@ -94,15 +105,17 @@ __global__ __launch_bounds__(kThreads) void butterfly_kernel(
   const uint32_t b = gtid % nb;
   const int64_t t = gtid / nb;
   if (t >= rows) return;
-  // first row in flight before the per-block set-up
-  const Raw<DT> first = load_raw<DT>(x, t * ldx + b * kBlk);
+  // parameter loads first: the set-up then waits for them only
+  const BlockParams bp = load_params(params, b);
+  __builtin_amdgcn_sched_barrier(0);
   BlockConsts c;
-  make_consts(params, b, c);
-  for_each_row<DT>(x, rows, ldx, b * kBlk, t, tstep, first, [&](float (&v)[kBlk], int64_t r) {
-    transform(v, c);
-    if (WRITE_Y) store_y(y + r * ldy + b * kBlk, v);
-    encode_store(v, q + r * ldq + b * (kBlk / 2), s + r * lds + b);
-  });
+  for_each_row<DT, kRowDepth>(
+      x, rows, ldx, b * kBlk, t, tstep, [&] { make_consts(bp, c); },
+      [&](float (&v)[kBlk], int64_t r) {
+        transform(v, c);
+        if (WRITE_Y) store_y(y + r * ldy + b * kBlk, v);
+        encode_store(v, q + r * ldq + b * (kBlk / 2), s + r * lds + b);
+      });
 }
 
 template <int DT, bool WRITE_Y>

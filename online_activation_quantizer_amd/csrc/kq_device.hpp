@@ -52,29 +52,48 @@ __device__ __forceinline__ void unpack(const Raw<DT_FP32>& r, float (&v)[kBlk]) 
 // consecutive (row, block) units, and since the lane count is a multiple of nb
 // each lane keeps one block column `col` (element offset) and walks rows t,
 // t + tstep, ... < rows, calling f(v, row) with the row's 32 values widened to
-// fp32.  `ra` holds row t, already loaded by the caller so that its latency
-// overlaps the caller's set-up work.  The loop is rotated so that the next row's
-// load is issued right after the current data is unpacked and stays in flight
-// during the whole transform, encode and store.  The prefetch is unconditional
-// (its row clamped to the last row, an in-bounds re-read), so no branch sits
-// around a memory operation and the compiler keeps exact counts of those in
-// flight.
-template <int DT, class F>
+// fp32.  The loads run DEPTH rows ahead in a ring of raw buffers.
+//  - The caller issues its own parameter loads before calling, so they are the
+//    oldest memory operations and `setup` (run after the first DEPTH rows are
+//    requested) waits for them only, not for the rows.
+//  - Each slot is refilled after its row has been transformed and stored, so the
+//    memory operations of every slot come in the same order (stores, then the
+//    refill).  The first round is peeled off the loop so that both edges into
+//    the loop header carry the same operations in flight; the compiler then
+//    waits for exactly the slot it needs and never for the stores.
+//  - Prefetches past the end are clamped to the last row (an in-bounds re-read),
+//    so no branch sits around a memory operation.
+template <int DT, int DEPTH, class S, class F>
 __device__ __forceinline__ void for_each_row(const void* __restrict__ x, int64_t rows, int64_t ldx,
-                                             int64_t col, int64_t t, int64_t tstep, Raw<DT> ra,
+                                             int64_t col, int64_t t, int64_t tstep, S&& setup,
                                              F&& f) {
   const int64_t last = rows - 1;
-  float v[kBlk];
-  unpack(ra, v);
-  int64_t tn = t + tstep;
-  ra = load_raw<DT>(x, (tn < last ? tn : last) * ldx + col);
-  for (;;) {
-    f(v, t);
-    if (tn > last) return;
-    t = tn;
-    tn = t + tstep;
-    unpack(ra, v);
-    ra = load_raw<DT>(x, (tn < last ? tn : last) * ldx + col);
+  Raw<DT> ring[DEPTH];
+#pragma unroll
+  for (int k = 0; k < DEPTH; ++k) {
+    const int64_t r = t + k * tstep;
+    ring[k] = load_raw<DT>(x, (r < last ? r : last) * ldx + col);
+  }
+  // keep the row loads behind the caller's parameter loads and ahead of the set-up
+  __builtin_amdgcn_sched_barrier(0);
+  setup();
+  __builtin_amdgcn_sched_barrier(0);
+  // one round over the ring; false once the rows are done
+  auto round = [&]() -> bool {
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) {
+      float v[kBlk];
+      unpack(ring[k], v);
+      f(v, t);
+      const int64_t rn = t + DEPTH * tstep;
+      ring[k] = load_raw<DT>(x, (rn < last ? rn : last) * ldx + col);
+      t += tstep;
+      if (t > last) return false;
+    }
+    return true;
+  };
+  if (!round()) return;
+  while (round()) {
   }
 }
 
@@ -127,8 +146,11 @@ __device__ __forceinline__ void encode_store(float (&y)[kBlk], uint8_t* __restri
     a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, y[8 * k + 6], y[8 * k + 7], sc, 3);
     w[k] = S == 255u ? 0u : a;
   }
-  *reinterpret_cast<uint4*>(qp) = make_uint4(w[0], w[1], w[2], w[3]);
-  *sp = (uint8_t)S;
+  // streaming stores: the codes are consumed by a later kernel, not re-read here
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 wv = {w[0], w[1], w[2], w[3]};
+  __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(qp));
+  __builtin_nontemporal_store((uint8_t)S, sp);
 }
 
 __device__ __forceinline__ void store_y(float* __restrict__ yp, const float (&y)[kBlk]) {

@@ -15,8 +15,15 @@
 // other 16 sit in lane l^32: the block amax and the packed code bytes are completed
 // with one cross-half exchange each.
 //
-// Each wave owns a pair of adjacent blocks (128 contiguous input bytes per token
-// row) and keeps their 12 A operands in VGPRs while it walks 32-row tiles.
+// Data flow.  A workgroup (4 waves) owns a group of 8 adjacent blocks and walks
+// 32-row tiles of them (32 rows x 512 contiguous bytes).  Its 256 threads load a
+// tile with fully coalesced 16-byte accesses into registers one tile ahead, park
+// it in LDS (double-buffered, 528-byte row pitch so the 32 rows of a column fall
+// on distinct banks) and each wave reads its two blocks' MFMA operands back with
+// ds_read_b128.  The 12 A operands of a wave's two blocks stay in VGPRs for the
+// whole walk.  Rows past the end and blocks past nb are clamped to the last row /
+// block: those lanes recompute and re-store exactly the bytes of the lane that
+// owns them, so no memory operation is predicated.
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
@@ -29,20 +36,23 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kMfmaBlocksPerCU = 2;
+constexpr int kTileRows = 32;
+constexpr int kTileBlocks = 8;                    // 2 per wave
+constexpr int kChunksPerRow = kTileBlocks * 4;    // 16-byte chunks per tile row
+constexpr int kPitch = kTileBlocks * 64 + 16;     // LDS row pitch in bytes
+constexpr int kTileBytes = kTileRows * kPitch;
+constexpr int kChunksPerThread = kTileRows * kChunksPerRow / kThreads;  // 4
 
-__device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
+constexpr int kMfmaBlocksPerCU = 3;  // resident workgroups per CU (LDS: 33 KB each)
 
 template <bool WRITE_Y>
-__device__ __forceinline__ void encode_tile(floatx16 acc, int h, bool store, uint8_t* qrow,
-                                            uint8_t* srow, float* yrow) {
+__device__ __forceinline__ void encode_tile(floatx16 acc, int h, uint8_t* qrow, uint8_t* srow,
+                                            float* yrow) {
   float m = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; r += 2) m = amax3(m, acc[r], acc[r + 1]);
   m = __builtin_elementwise_maximum(m, __shfl_xor(m, 32));
-  if (WRITE_Y && store) {
+  if (WRITE_Y) {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       *reinterpret_cast<float4*>(yrow + 8 * g + 4 * h) =
@@ -73,81 +83,106 @@ __device__ __forceinline__ void encode_tile(floatx16 acc, int h, bool store, uin
   const uint32_t lo = h ? recv : w0, hi = h ? w1 : recv;
   const uint32_t o0 = (lo & 0xFFFFu) | (hi << 16);
   const uint32_t o1 = (lo >> 16) | (hi & 0xFFFF0000u);
-  if (store) {
-    *reinterpret_cast<uint2*>(qrow + 8 * h) = make_uint2(o0, o1);
-    if (h == 0) *srow = (uint8_t)S;
-  }
+  *reinterpret_cast<uint2*>(qrow + 8 * h) = make_uint2(o0, o1);
+  if (h == 0) *srow = (uint8_t)S;
 }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 template <bool WRITE_Y>
 __global__ __launch_bounds__(kThreads) void mfma_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t nb, int64_t ldx,
+    const uint16_t* __restrict__ x, int64_t rows, uint32_t nb, int64_t ldx,
     const uint16_t* __restrict__ T3, uint8_t* __restrict__ q, int64_t ldq,
     uint8_t* __restrict__ s, int64_t lds, float* __restrict__ y, int64_t ldy, uint32_t tstep) {
-  const int lane = threadIdx.x & 63;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTileBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
-  // the wave count gridDim.x * 4 is a multiple of npair (tstep tiles per pass)
-  const uint32_t wave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const uint32_t npair = (uint32_t)((nb + 1) / 2);
-  const uint32_t pair = wave % npair;
-  const int64_t ntiles = (rows + 31) / 32;
-  int64_t tile = wave / npair;
-  if (tile >= ntiles) return;
+  // the grid is a multiple of the block-group count (tstep tiles per pass)
+  const uint32_t ngroups = (nb + kTileBlocks - 1) / kTileBlocks;
+  const uint32_t bg = blockIdx.x % ngroups;
+  uint32_t rt = blockIdx.x / ngroups;
+  const uint32_t ntiles = (uint32_t)((rows + kTileRows - 1) / kTileRows);
+  if (rt >= ntiles) return;
+  const int64_t last = rows - 1;
 
-  const int64_t b0 = 2 * (int64_t)pair;
-  const bool has2 = b0 + 1 < nb;
-  int64_t bb[2] = {b0, has2 ? b0 + 1 : b0};
+  // this thread's 4 tile chunks: rows (tid/32) + 8 i, chunk column tid % 32
+  const int ccol = tid & (kChunksPerRow - 1);
+  uint32_t cblk = bg * kTileBlocks + (ccol >> 2);
+  if (cblk > nb - 1) cblk = nb - 1;
+  const int64_t ccol_elem = (int64_t)cblk * kBlk + (ccol & 3) * 8;
+  const int crow0 = tid / kChunksPerRow;
+  uint4 R[kChunksPerThread];
+  auto load_tile = [&](uint32_t t_idx) {
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      int64_t row = (int64_t)t_idx * kTileRows + crow0 + 8 * i;
+      row = row < last ? row : last;
+      R[i] = *reinterpret_cast<const uint4*>(x + row * ldx + ccol_elem);
+    }
+  };
+  load_tile(rt);
 
-  // A operands: [block][split hi/mid/lo][K half]
+  // A operands of this wave's two blocks: [block][split hi/mid/lo][K half]
+  uint32_t blk[2];
   bf16x8 A[2][3][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t b = bg * kTileBlocks + 2 * wave + j;
+    blk[j] = b < nb ? b : nb - 1;
 #pragma unroll
     for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
-        A[j][sp][kh] = load8(T3 + (sp * nb + bb[j]) * 1024 + n * 32 + 16 * kh + 8 * h);
+        A[j][sp][kh] = *reinterpret_cast<const bf16x8*>(
+            T3 + ((size_t)sp * nb + blk[j]) * 1024 + n * 32 + 16 * kh + 8 * h);
+  }
 
-  for (; tile < ntiles; tile += tstep) {
-    const int64_t t = tile * 32 + n;
-    const bool valid = t < rows;
-    const int64_t tl = valid ? t : rows - 1;  // tail lanes re-read a valid row, store nothing
-    bf16x8 B[2][2];
+  int buf = 0;
+  for (;;) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) B[j][kh] = load8(x + tl * ldx + 32 * bb[j] + 16 * kh + 8 * h);
+    for (int i = 0; i < kChunksPerThread; ++i)
+      *reinterpret_cast<uint4*>(&tile[buf][(crow0 + 8 * i) * kPitch + ccol * 16]) = R[i];
+    __syncthreads();
+    const uint32_t rn = rt + tstep;
+    // next tile in flight during the math (clamped: the last pass re-reads a valid tile)
+    load_tile(rn < ntiles ? rn : rt);
+
+    int64_t t = (int64_t)rt * kTileRows + n;
+    t = t < last ? t : last;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      const int jb = 2 * wave + j;
+      const uint8_t* src = &tile[buf][n * kPitch + jb * 64 + 16 * h];
+      const bf16x8 B0 = as_bf16x8(*reinterpret_cast<const uint4*>(src));
+      const bf16x8 B1 = as_bf16x8(*reinterpret_cast<const uint4*>(src + 32));
       floatx16 acc = {};
       // smallest parts first
 #pragma unroll
-      for (int sp = 2; sp >= 0; --sp)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[j][sp][kh], B[j][kh], acc, 0, 0, 0);
-      const bool store = valid && (j == 0 || has2);
-      encode_tile<WRITE_Y>(acc, h, store, q + t * ldq + 16 * bb[j], s + t * lds + bb[j],
-                           WRITE_Y ? y + t * ldy + 32 * bb[j] : nullptr);
+      for (int sp = 2; sp >= 0; --sp) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[j][sp][0], B0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[j][sp][1], B1, acc, 0, 0, 0);
+      }
+      encode_tile<WRITE_Y>(acc, h, q + t * ldq + 16 * blk[j], s + t * lds + blk[j],
+                           WRITE_Y ? y + t * ldy + 32 * blk[j] : nullptr);
     }
+    if (rn >= ntiles) return;
+    rt = rn;
+    buf ^= 1;
   }
 }
 
 template <bool WRITE_Y>
 hipError_t launch_t(const LaunchArgs& a) {
-  const int64_t npair = (a.nb + 1) / 2;
-  const int64_t waves_per_wg = kThreads / 64;
-  const int64_t m = npair / gcd64(npair, waves_per_wg);  // grid granule
-  const int64_t ntiles = (a.rows + 31) / 32;
-  const int64_t need = (npair * ntiles + waves_per_wg - 1) / waves_per_wg;
+  const int64_t ngroups = (a.nb + kTileBlocks - 1) / kTileBlocks;
+  const int64_t ntiles = (a.rows + kTileRows - 1) / kTileRows;
   int64_t target = (int64_t)a.cus * kMfmaBlocksPerCU;
-  if (target > need) target = need;
-  int64_t k = (target + m - 1) / m;
+  if (target > ngroups * ntiles) target = ngroups * ntiles;
+  int64_t k = (target + ngroups - 1) / ngroups;
   if (k < 1) k = 1;
-  const uint32_t tstep = (uint32_t)(k * m * waves_per_wg / npair);
-  hipLaunchKernelGGL((mfma_kernel<WRITE_Y>), dim3((unsigned)(k * m)), dim3(kThreads), 0,
-                     (hipStream_t)a.stream, (const uint16_t*)a.x, a.rows, a.nb, a.ldx,
-                     (const uint16_t*)a.t, a.q, a.ldq, a.s, a.lds, a.y, a.ldy, tstep);
+  hipLaunchKernelGGL((mfma_kernel<WRITE_Y>), dim3((unsigned)(k * ngroups)), dim3(kThreads), 0,
+                     (hipStream_t)a.stream, (const uint16_t*)a.x, a.rows, (uint32_t)a.nb, a.ldx,
+                     (const uint16_t*)a.t, a.q, a.ldq, a.s, a.lds, a.y, a.ldy, (uint32_t)k);
   return hipGetLastError();
 }
 

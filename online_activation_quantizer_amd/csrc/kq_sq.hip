@@ -22,25 +22,32 @@ __global__ __launch_bounds__(kThreads) void sq_kernel(
   const uint32_t b = gtid % nb;
   const int64_t t = gtid / nb;
   if (t >= rows) return;
-  const Raw<DT> first = load_raw<DT>(x, t * ldx + b * kBlk);
-  float m[kBlk];
+  // multiplier loads first: they complete before the rows
+  float4 mr[8];
   {
     const float4* mp = reinterpret_cast<const float4*>(mult + (size_t)b * kBlk);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float4 f = mp[k];
-      m[4 * k] = f.x;
-      m[4 * k + 1] = f.y;
-      m[4 * k + 2] = f.z;
-      m[4 * k + 3] = f.w;
-    }
+    for (int k = 0; k < 8; ++k) mr[k] = mp[k];
   }
-  for_each_row<DT>(x, rows, ldx, b * kBlk, t, tstep, first, [&](float (&v)[kBlk], int64_t r) {
+  __builtin_amdgcn_sched_barrier(0);
+  float m[kBlk];
+  for_each_row<DT, kRowDepth>(
+      x, rows, ldx, b * kBlk, t, tstep,
+      [&] {
 #pragma unroll
-    for (int i = 0; i < kBlk; ++i) v[i] *= m[i];
-    if (WRITE_Y) store_y(y + r * ldy + b * kBlk, v);
-    encode_store(v, q + r * ldq + b * (kBlk / 2), s + r * lds + b);
-  });
+        for (int k = 0; k < 8; ++k) {
+          m[4 * k] = mr[k].x;
+          m[4 * k + 1] = mr[k].y;
+          m[4 * k + 2] = mr[k].z;
+          m[4 * k + 3] = mr[k].w;
+        }
+      },
+      [&](float (&v)[kBlk], int64_t r) {
+#pragma unroll
+        for (int i = 0; i < kBlk; ++i) v[i] *= m[i];
+        if (WRITE_Y) store_y(y + r * ldy + b * kBlk, v);
+        encode_store(v, q + r * ldq + b * (kBlk / 2), s + r * lds + b);
+      });
 }
 
 template <int DT, bool WRITE_Y>

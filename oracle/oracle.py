@@ -15,6 +15,8 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle_kq.so")
+# The mutation tests point the pins at deliberately broken builds of the oracle.
+_LIB_OVERRIDE = os.environ.get("KQ_ORACLE_LIB")
 SOURCES = [os.path.join(HERE, "kq_oracle.cpp")]
 
 BF16, FP32 = 0, 1
@@ -36,9 +38,10 @@ def build(force: bool = True) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        path = _LIB_OVERRIDE or LIB_PATH
+        if not _LIB_OVERRIDE and not os.path.exists(LIB_PATH):
             build()
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         P, I64, I, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
         L.oq_factor.argtypes = [D, D, D, P]
         L.oq_factor_inverse.argtypes = [D, D, D, P]

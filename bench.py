@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-sq", action="store_true", help="skip the SmoothQuant baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from Python instead of replaying a captured graph")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (4 times) as the "
                          "known-size reference for hardware byte counters")
@@ -56,6 +58,37 @@ def timed(fn, steps, warmup, stream):
         fn(i)
     end.record(stream)
     end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def timed_graph(fn, steps, warmup):
+    """Average milliseconds per step when exactly `steps` steps (fn(0) .. fn(steps-1))
+    are replayed from one captured HIP graph.  The graph holds the same kernel
+    launches on the same buffers as the eager loop; it only removes the per-launch
+    host work.  One untimed replay (after `warmup` eager steps) precedes the timed one."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(max(1, warmup)):
+            fn(i)
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        g.replay()
+        side.synchronize()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(side)
+        g.replay()
+        end.record(side)
+        end.synchronize()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
 
@@ -149,8 +182,12 @@ def main():
         j = i % P
         kq.sq_quantize(xs[j], m_dev, q=qs[j], s=ss[j])
 
-    ms = timed(kq_step, args.steps, args.warmup, stream)
-    sq_ms = None if args.no_sq else timed(sq_step, args.steps, args.warmup, stream)
+    if args.eager:
+        ms = timed(kq_step, args.steps, args.warmup, stream)
+        sq_ms = None if args.no_sq else timed(sq_step, args.steps, args.warmup, stream)
+    else:
+        ms = timed_graph(kq_step, args.steps, args.warmup)
+        sq_ms = None if args.no_sq else timed_graph(sq_step, args.steps, args.warmup)
 
     # parity of one production step against the oracle
     parity = None
@@ -181,7 +218,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"FLUX.1-schnell-like joint-stream activations {rows}x{d} bf16, "
                                f"{nb} factor sets, {args.variant}",
-                   "rows": rows, "d": d, "input": "bf16", "pool_sets": P},
+                   "rows": rows, "d": d, "input": "bf16", "pool_sets": P,
+                   "launch": "eager" if args.eager else "hip graph replay"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic() if args.variant == "butterfly" else None},

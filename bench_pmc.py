@@ -3,9 +3,9 @@
 the quantizer kernel, calibrated against a plain copy of known size.
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o fetch -- \\
-        python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --calib-copy-mib 256
+        python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --eager --calib-copy-mib 256
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o write -- \\
-        python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --calib-copy-mib 256
+        python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --eager --calib-copy-mib 256
     python3 bench_pmc.py DIR 256
 
 FETCH_SIZE / WRITE_SIZE are read in KiB per dispatch.  The copy kernel reads and
@@ -69,8 +69,8 @@ def main():
     json.dump(res, open(bench.TRAFFIC_FILE, "w"), indent=1)
     md = ["# HBM traffic of kq_quantize (butterfly), 4608x3072 bf16", "",
           "Commands (repository root, one MI355X):", "", "```",
-          "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch -o fetch -- python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --calib-copy-mib %d" % mib,
-          "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write -o write -- python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --calib-copy-mib %d" % mib,
+          "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch -o fetch -- python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --eager --calib-copy-mib %d" % mib,
+          "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write -o write -- python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --eager --calib-copy-mib %d" % mib,
           "python3 bench_pmc.py gpurun_out/pmc %d" % mib, "```", "",
           "| | counter (KiB/dispatch) | scale from the %d MiB copy | bytes per launch | algorithmic bytes |" % mib,
           "|---|---|---|---|---|",

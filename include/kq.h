@@ -39,8 +39,9 @@
  *     returns a negative kq_status and enqueues nothing.  KQ_ERR_HIP means a
  *     launch failed; kq_last_hip_error() gives the hipError_t (per thread).
  *     Nothing is printed and no exception crosses the ABI.
- *   - rows == 0 is a no-op that returns KQ_OK.  d must be a positive multiple of
- *     32 and at most 2^27 (2^22 blocks).  x, q and their row pitches (in bytes) must be 16-byte aligned.
+ *   - rows == 0 is a no-op that returns KQ_OK.  rows < 2^31; d must be a positive
+ *     multiple of 32 and at most 2^27 (2^22 blocks); every row pitch must be below
+ *     4 GiB.  x, q and their row pitches (in bytes) must be 16-byte aligned.
  *   - Factor parameters must be finite with u != 0; otherwise the output is
  *     unspecified (checking would cost a device pass).  Inputs are expected to be
  *     finite; the NaN/Inf scale rule above is best effort.
@@ -58,8 +59,9 @@ extern "C" {
 typedef enum {
   KQ_OK = 0,
   KQ_ERR_NULL = -1,     /* a required pointer is NULL                       */
-  KQ_ERR_SHAPE = -2,    /* negative rows, d not a positive multiple of 32
-                           (or above 2^27), a pitch smaller than the row     */
+  KQ_ERR_SHAPE = -2,    /* rows negative or >= 2^31, d not a positive
+                           multiple of 32 (or above 2^27), a pitch smaller
+                           than the row or of 4 GiB and more                 */
   KQ_ERR_ALIGN = -3,    /* x, q (or a pitch in bytes) not 16-byte aligned   */
   KQ_ERR_DTYPE = -4,    /* unknown input dtype                              */
   KQ_ERR_FORMAT = -5,   /* unknown transform format, or one the variant

@@ -42,8 +42,11 @@ int current_cus(int* cus) {
   return KQ_OK;
 }
 
-// Kernels index lanes with 32-bit arithmetic: at most 2^22 blocks (d <= 2^27).
+// Kernels index lanes, rows and row pitches with 32-bit arithmetic: at most 2^22
+// blocks (d <= 2^27), rows < 2^31 and row pitches below 4 GiB.
 constexpr int64_t kMaxBlocks = int64_t(1) << 22;
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxPitch = (int64_t(1) << 32) - 1;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -55,7 +58,9 @@ int check_common(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
   if (dtype != KQ_BF16 && dtype != KQ_FP32) return KQ_ERR_DTYPE;
   if (rows < 0 || d <= 0 || d % 32 != 0 || ldx < d || ldq < d / 2 || lds < d / 32)
     return KQ_ERR_SHAPE;
-  if (d / 32 > kMaxBlocks) return KQ_ERR_SHAPE;
+  if (d / 32 > kMaxBlocks || rows > kMaxRows || ldx * elem_size(dtype) > kMaxPitch ||
+      ldq > kMaxPitch || lds > kMaxPitch)
+    return KQ_ERR_SHAPE;
   if (rows == 0) return KQ_OK;
   if (!x || !t || !q || !s) return KQ_ERR_NULL;
   if (!aligned(x, 16) || (ldx * elem_size(dtype)) % 16 != 0 || !aligned(q, 16) || ldq % 16 != 0)
@@ -94,7 +99,7 @@ int quantize_impl(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx
   rc = resolve_variant(variant, tfmt, &v);
   if (rc != KQ_OK) return rc;
   if (debug) {
-    if (ldy < d) return KQ_ERR_SHAPE;
+    if (ldy < d || ldy * 4 > kMaxPitch) return KQ_ERR_SHAPE;
     if (rows > 0 && !y) return KQ_ERR_NULL;
     if (rows > 0 && !aligned(y, 4)) return KQ_ERR_ALIGN;
   }
@@ -115,7 +120,7 @@ int sq_impl(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, cons
   int rc = check_common(x, dtype, rows, d, ldx, mult, q, ldq, s, lds);
   if (rc != KQ_OK) return rc;
   if (debug) {
-    if (ldy < d) return KQ_ERR_SHAPE;
+    if (ldy < d || ldy * 4 > kMaxPitch) return KQ_ERR_SHAPE;
     if (rows > 0 && !y) return KQ_ERR_NULL;
     if (rows > 0 && !aligned(y, 4)) return KQ_ERR_ALIGN;
   }

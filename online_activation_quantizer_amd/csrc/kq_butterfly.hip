@@ -57,7 +57,7 @@ __device__ __forceinline__ void make_consts(const BlockParams& bp, BlockConsts& 
   for (int k = 0; k < 5; ++k) {
     const float l = bp.p[3 * k + 0], uk = bp.p[3 * k + 1], v = bp.p[3 * k + 2];
     u[k] = uk;
-    iu[k] = 1.0f / uk;
+    iu[k] = __builtin_amdgcn_rcpf(uk);  // within 1 ulp; exact for powers of two
     c.su[k] = uk * v;
     c.ll[k] = l;
   }
@@ -97,24 +97,29 @@ __device__ __forceinline__ void transform(float (&v)[kBlk], const BlockConsts& c
 
 template <int DT, bool WRITE_Y>
 __global__ __launch_bounds__(kThreads) void butterfly_kernel(
-    const void* __restrict__ x, int64_t rows, uint32_t nb, int64_t ldx, uint32_t tstep,
-    const float* __restrict__ params, uint8_t* __restrict__ q, int64_t ldq,
-    uint8_t* __restrict__ s, int64_t lds, float* __restrict__ y, int64_t ldy) {
-  // the lane count gridDim.x * kThreads is a multiple of nb (tstep rows per pass)
+    const uint8_t* __restrict__ x, uint32_t rows, uint32_t nb, uint32_t ldx, uint32_t tstep,
+    const float* __restrict__ params, uint8_t* __restrict__ q, uint32_t ldq,
+    uint8_t* __restrict__ s, uint32_t lds, float* __restrict__ y, uint32_t ldy) {
+  // the lane count gridDim.x * kThreads is a multiple of nb (tstep rows per pass);
+  // pitches are in bytes
   const uint32_t gtid = blockIdx.x * kThreads + threadIdx.x;
   const uint32_t b = gtid % nb;
-  const int64_t t = gtid / nb;
+  const uint32_t t = gtid / nb;
   if (t >= rows) return;
   // parameter loads first: the set-up then waits for them only
   const BlockParams bp = load_params(params, b);
   __builtin_amdgcn_sched_barrier(0);
   BlockConsts c;
+  uint8_t* const qcol = q + b * (kBlk / 2);
+  uint8_t* const scol = s + b;
+  uint8_t* const ycol = reinterpret_cast<uint8_t*>(y) + b * kBlk * 4;
   for_each_row<DT, kRowDepth>(
-      x, rows, ldx, b * kBlk, t, tstep, [&] { make_consts(bp, c); },
-      [&](float (&v)[kBlk], int64_t r) {
+      x + (size_t)b * kBlk * (DT == DT_BF16 ? 2 : 4), rows, ldx, t, tstep,
+      [&] { make_consts(bp, c); },
+      [&](float (&v)[kBlk], uint32_t r) {
         transform(v, c);
-        if (WRITE_Y) store_y(y + r * ldy + b * kBlk, v);
-        encode_store(v, q + r * ldq + b * (kBlk / 2), s + r * lds + b);
+        if (WRITE_Y) store_y(reinterpret_cast<float*>(ycol + (uint64_t)r * ldy), v);
+        encode_store(v, qcol + (uint64_t)r * ldq, scol + (uint64_t)r * lds);
       });
 }
 
@@ -122,9 +127,11 @@ template <int DT, bool WRITE_Y>
 hipError_t launch_t(const LaunchArgs& a) {
   uint32_t tstep = 0;
   const int64_t grid = grid_for_units(a.rows, a.nb, a.cus, kBlocksPerCU, &tstep);
+  const int64_t esz = DT == DT_BF16 ? 2 : 4;
   hipLaunchKernelGGL((butterfly_kernel<DT, WRITE_Y>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     (hipStream_t)a.stream, a.x, a.rows, (uint32_t)a.nb, a.ldx, tstep,
-                     (const float*)a.t, a.q, a.ldq, a.s, a.lds, a.y, a.ldy);
+                     (hipStream_t)a.stream, (const uint8_t*)a.x, (uint32_t)a.rows,
+                     (uint32_t)a.nb, (uint32_t)(a.ldx * esz), tstep, (const float*)a.t, a.q,
+                     (uint32_t)a.ldq, a.s, (uint32_t)a.lds, a.y, (uint32_t)(a.ldy * 4));
   return hipGetLastError();
 }
 

@@ -17,12 +17,11 @@ template <> struct Raw<DT_BF16> { uint4 w[4]; };
 template <> struct Raw<DT_FP32> { uint4 w[8]; };
 
 template <int DT>
-__device__ __forceinline__ Raw<DT> load_raw(const void* x, int64_t elem_off) {
+__device__ __forceinline__ Raw<DT> load_raw(const uint8_t* p) {
   Raw<DT> r;
-  const uint4* p = reinterpret_cast<const uint4*>(
-      static_cast<const char*>(x) + elem_off * (DT == DT_BF16 ? 2 : 4));
+  const uint4* v = reinterpret_cast<const uint4*>(p);
 #pragma unroll
-  for (int k = 0; k < (int)(sizeof(r.w) / sizeof(uint4)); ++k) r.w[k] = p[k];
+  for (int k = 0; k < (int)(sizeof(r.w) / sizeof(uint4)); ++k) r.w[k] = v[k];
   return r;
 }
 
@@ -50,30 +49,31 @@ __device__ __forceinline__ void unpack(const Raw<DT_FP32>& r, float (&v)[kBlk]) 
 
 // Row walker.  Lane-to-unit mapping is row-major: the grid's lanes cover
 // consecutive (row, block) units, and since the lane count is a multiple of nb
-// each lane keeps one block column `col` (element offset) and walks rows t,
-// t + tstep, ... < rows, calling f(v, row) with the row's 32 values widened to
-// fp32.  The loads run DEPTH rows ahead in a ring of raw buffers.
+// each lane keeps one block column and walks rows t, t + tstep, ... < rows,
+// calling f(v, row) with the row's 32 values widened to fp32.  `xcol` points at
+// the lane's block column in row 0 and `ldx` is the row pitch in bytes; row
+// arithmetic is 32-bit, so every address is one multiply-add.  The loads run
+// DEPTH rows ahead in a ring of raw buffers.
 //  - The caller issues its own parameter loads before calling, so they are the
 //    oldest memory operations and `setup` (run after the first DEPTH rows are
 //    requested) waits for them only, not for the rows.
-//  - Each slot is refilled after its row has been transformed and stored, so the
-//    memory operations of every slot come in the same order (stores, then the
-//    refill).  The first round is peeled off the loop so that both edges into
-//    the loop header carry the same operations in flight; the compiler then
-//    waits for exactly the slot it needs and never for the stores.
+//  - Each slot is refilled right after it is unpacked, before its row's math and
+//    stores, so a refill is in flight during DEPTH rows of work and the memory
+//    operations of every slot come in the same order (refill, then stores).  The
+//    first round is peeled off the loop so that both edges into the loop header
+//    carry the same operations in flight; the compiler then waits for exactly
+//    the slot it needs and never for the stores.
 //  - Prefetches past the end are clamped to the last row (an in-bounds re-read),
 //    so no branch sits around a memory operation.
 template <int DT, int DEPTH, class S, class F>
-__device__ __forceinline__ void for_each_row(const void* __restrict__ x, int64_t rows, int64_t ldx,
-                                             int64_t col, int64_t t, int64_t tstep, S&& setup,
+__device__ __forceinline__ void for_each_row(const uint8_t* __restrict__ xcol, uint32_t rows,
+                                             uint32_t ldx, uint32_t t, uint32_t tstep, S&& setup,
                                              F&& f) {
-  const int64_t last = rows - 1;
+  const uint32_t last = rows - 1;
+  auto row_ptr = [&](uint32_t r) { return xcol + (uint64_t)(r < last ? r : last) * ldx; };
   Raw<DT> ring[DEPTH];
 #pragma unroll
-  for (int k = 0; k < DEPTH; ++k) {
-    const int64_t r = t + k * tstep;
-    ring[k] = load_raw<DT>(x, (r < last ? r : last) * ldx + col);
-  }
+  for (int k = 0; k < DEPTH; ++k) ring[k] = load_raw<DT>(row_ptr(t + k * tstep));
   // keep the row loads behind the caller's parameter loads and ahead of the set-up
   __builtin_amdgcn_sched_barrier(0);
   setup();
@@ -84,10 +84,13 @@ __device__ __forceinline__ void for_each_row(const void* __restrict__ x, int64_t
     for (int k = 0; k < DEPTH; ++k) {
       float v[kBlk];
       unpack(ring[k], v);
+      ring[k] = load_raw<DT>(row_ptr(t + DEPTH * tstep));
+      // pins the refill ahead of this row's math and stores: without the barrier the
+      // compiler folds the ring's incoming loads into one load at the top of the
+      // next round (or moves it behind the stores), which removes the prefetch
+      __builtin_amdgcn_sched_barrier(0);
       f(v, t);
-      const int64_t rn = t + DEPTH * tstep;
-      ring[k] = load_raw<DT>(x, (rn < last ? rn : last) * ldx + col);
-      t += tstep;
+      t += tstep;  // rows < 2^31 and tstep < 2^24: no wrap
       if (t > last) return false;
     }
     return true;

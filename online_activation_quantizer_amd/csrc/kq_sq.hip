@@ -15,12 +15,12 @@ namespace {
 
 template <int DT, bool WRITE_Y>
 __global__ __launch_bounds__(kThreads) void sq_kernel(
-    const void* __restrict__ x, int64_t rows, uint32_t nb, int64_t ldx, uint32_t tstep,
-    const float* __restrict__ mult, uint8_t* __restrict__ q, int64_t ldq,
-    uint8_t* __restrict__ s, int64_t lds, float* __restrict__ y, int64_t ldy) {
+    const uint8_t* __restrict__ x, uint32_t rows, uint32_t nb, uint32_t ldx, uint32_t tstep,
+    const float* __restrict__ mult, uint8_t* __restrict__ q, uint32_t ldq,
+    uint8_t* __restrict__ s, uint32_t lds, float* __restrict__ y, uint32_t ldy) {
   const uint32_t gtid = blockIdx.x * kThreads + threadIdx.x;
   const uint32_t b = gtid % nb;
-  const int64_t t = gtid / nb;
+  const uint32_t t = gtid / nb;
   if (t >= rows) return;
   // multiplier loads first: they complete before the rows
   float4 mr[8];
@@ -31,8 +31,11 @@ __global__ __launch_bounds__(kThreads) void sq_kernel(
   }
   __builtin_amdgcn_sched_barrier(0);
   float m[kBlk];
+  uint8_t* const qcol = q + b * (kBlk / 2);
+  uint8_t* const scol = s + b;
+  uint8_t* const ycol = reinterpret_cast<uint8_t*>(y) + b * kBlk * 4;
   for_each_row<DT, kRowDepth>(
-      x, rows, ldx, b * kBlk, t, tstep,
+      x + (size_t)b * kBlk * (DT == DT_BF16 ? 2 : 4), rows, ldx, t, tstep,
       [&] {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -42,11 +45,11 @@ __global__ __launch_bounds__(kThreads) void sq_kernel(
           m[4 * k + 3] = mr[k].w;
         }
       },
-      [&](float (&v)[kBlk], int64_t r) {
+      [&](float (&v)[kBlk], uint32_t r) {
 #pragma unroll
         for (int i = 0; i < kBlk; ++i) v[i] *= m[i];
-        if (WRITE_Y) store_y(y + r * ldy + b * kBlk, v);
-        encode_store(v, q + r * ldq + b * (kBlk / 2), s + r * lds + b);
+        if (WRITE_Y) store_y(reinterpret_cast<float*>(ycol + (uint64_t)r * ldy), v);
+        encode_store(v, qcol + (uint64_t)r * ldq, scol + (uint64_t)r * lds);
       });
 }
 
@@ -54,9 +57,11 @@ template <int DT, bool WRITE_Y>
 hipError_t launch_t(const LaunchArgs& a) {
   uint32_t tstep = 0;
   const int64_t grid = grid_for_units(a.rows, a.nb, a.cus, kBlocksPerCU, &tstep);
+  const int64_t esz = DT == DT_BF16 ? 2 : 4;
   hipLaunchKernelGGL((sq_kernel<DT, WRITE_Y>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     (hipStream_t)a.stream, a.x, a.rows, (uint32_t)a.nb, a.ldx, tstep,
-                     (const float*)a.t, a.q, a.ldq, a.s, a.lds, a.y, a.ldy);
+                     (hipStream_t)a.stream, (const uint8_t*)a.x, (uint32_t)a.rows,
+                     (uint32_t)a.nb, (uint32_t)(a.ldx * esz), tstep, (const float*)a.t, a.q,
+                     (uint32_t)a.ldq, a.s, (uint32_t)a.lds, a.y, (uint32_t)(a.ldy * 4));
   return hipGetLastError();
 }
 

@@ -279,6 +279,47 @@ int oq_sq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ld
   return rc;
 }
 
+int oq_weight_transform(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
+                        const float* params, double* w_out) {
+  if (rows == 0 && !bad_shape(rows, d, ldw)) return 0;
+  if (!w || !params || !w_out || bad_shape(rows, d, ldw) || (dtype != OQ_BF16 && dtype != OQ_FP32))
+    return -1;
+  const int64_t nb = d / kBlk;
+  std::vector<double> Ti((size_t)nb * kBlk * kBlk);
+  oq_expand(params, nb, 1, Ti.data());  // kron of the factor inverses = T_b^-1
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b) {
+      double wb[kBlk];
+      for (int i = 0; i < kBlk; ++i) wb[i] = oq_load(w, dtype, r * ldw + b * kBlk + i);
+      const double* Tb = Ti.data() + b * kBlk * kBlk;
+      for (int j = 0; j < kBlk; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < kBlk; ++i) acc += wb[i] * Tb[i * kBlk + j];
+        w_out[r * d + b * kBlk + j] = acc;
+      }
+    }
+  return 0;
+}
+
+int oq_quantize_weights(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
+                        const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                        double* w_out, int nthreads) {
+  if (!w || !params || !q || !s || bad_shape(rows, d, ldw) ||
+      (dtype != OQ_BF16 && dtype != OQ_FP32) || ldq < d / 2 || lds < d / kBlk)
+    return -1;
+  int rc = 0;
+  parallel_rows(rows, nthreads, [&](int64_t r0, int64_t r1) {
+    const int64_t n = r1 - r0;
+    std::vector<double> buf;
+    double* y = w_out ? w_out + r0 * d : (buf.resize((size_t)n * d), buf.data());
+    const uint8_t* base = (const uint8_t*)w + r0 * ldw * (dtype == OQ_BF16 ? 2 : 4);
+    if (oq_weight_transform(base, dtype, n, d, ldw, params, y) != 0 ||
+        oq_encode(y, n, d, q + r0 * ldq, ldq, s + r0 * lds, lds) != 0)
+      rc = -1;
+  });
+  return rc;
+}
+
 }  // extern "C"
 
 namespace {

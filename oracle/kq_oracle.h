@@ -100,6 +100,17 @@ int oq_sq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ld
                    const float* mult, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
                    double* y_out, int nthreads);
 
+/* Weight side: W'[r][32b+j] = sum_i W[r][32b+i] * Tinv_b[i][j], i.e. W' = W T^-1 with
+ * T^-1 block-diagonal (the inverse folded into the weights, so that W' (T x) = W x).
+ * [ABS]  w is [rows][ldw] of dtype; w_out [rows][d] fp64. */
+int oq_weight_transform(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
+                        const float* params, double* w_out);
+
+/* W' followed by the MXFP4 encoding along d (blocks of 32 input channels). */
+int oq_quantize_weights(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
+                        const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                        double* w_out, int nthreads);
+
 /* Parity accounting of candidate outputs against the oracle's fp64 values y_o.
  * Per block the tolerance is tol_coef * max|x_blk| (tol_mode 0, the fp32 rule) or
  * tol_coef * max|y_o_blk| (tol_mode 1, the block-relative bf16 rule).

@@ -58,6 +58,8 @@ def lib():
         L.oq_encode.argtypes = [P, I64, I64, P, I64, P, I64]
         L.oq_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
         L.oq_sq_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
+        L.oq_weight_transform.argtypes = [P, I, I64, I64, I64, P, P]
+        L.oq_quantize_weights.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
         L.oq_classify.argtypes = [P, I, I64, I64, I64, P, I, D, P, I64, P, I64, P, I64, P]
         _lib = L
     return _lib
@@ -184,6 +186,30 @@ def sq_quantize(x: np.ndarray, mult: np.ndarray, want_y: bool = False, nthreads:
     rc = lib().oq_sq_quantize(_ptr(x), dt, rows, d, ldx, _ptr(m), _ptr(q), d // 2, _ptr(s), d // 32,
                               _ptr(y) if want_y else None, nthreads)
     _check(rc, "sq_quantize")
+    return q, s, y
+
+
+def weight_transform(w: np.ndarray, params: np.ndarray) -> np.ndarray:
+    """W' = W T^-1 (block-diagonal), fp64 [rows, d]."""
+    dt, rows, ldw = _x_info(w)
+    d = w.shape[1]
+    p = np.ascontiguousarray(params, np.float32)
+    out = np.zeros((rows, d), np.float64)
+    _check(lib().oq_weight_transform(_ptr(w), dt, rows, d, ldw, _ptr(p), _ptr(out)), "weight_transform")
+    return out
+
+
+def quantize_weights(w: np.ndarray, params: np.ndarray, want_y: bool = False, nthreads: int = 0):
+    """(q [rows, d/2], s [rows, d/32], W' fp64 or None): MXFP4 of W T^-1 along d."""
+    dt, rows, ldw = _x_info(w)
+    d = w.shape[1]
+    p = np.ascontiguousarray(params, np.float32)
+    q = np.zeros((rows, d // 2), np.uint8)
+    s = np.zeros((rows, d // 32), np.uint8)
+    y = np.zeros((rows, d), np.float64) if want_y else None
+    rc = lib().oq_quantize_weights(_ptr(w), dt, rows, d, ldw, _ptr(p), _ptr(q), d // 2, _ptr(s), d // 32,
+                                   _ptr(y) if want_y else None, nthreads)
+    _check(rc, "quantize_weights")
     return q, s, y
 
 

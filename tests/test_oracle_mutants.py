@@ -52,6 +52,9 @@ MUTANTS = {
     "nibbles_swapped": (
         "qb[i / 2] = (uint8_t)(oq_e2m1_code(yb[i], e) | (oq_e2m1_code(yb[i + 1], e) << 4));",
         "qb[i / 2] = (uint8_t)(oq_e2m1_code(yb[i + 1], e) | (oq_e2m1_code(yb[i], e) << 4));"),
+    "weight_side_transposed": (
+        "for (int i = 0; i < kBlk; ++i) acc += wb[i] * Tb[i * kBlk + j];",
+        "for (int i = 0; i < kBlk; ++i) acc += wb[i] * Tb[j * kBlk + i];"),
     "amax_without_abs": (
         "        amax = std::max(amax, std::fabs(yb[i]));\n      }\n      uint8_t* qb",
         "        amax = std::max(amax, yb[i]);\n      }\n      uint8_t* qb"),

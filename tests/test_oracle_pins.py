@@ -286,3 +286,40 @@ def test_classify_counts_planted_mismatches(oq):
     st = oq.classify(x, y, q, s, 0, 1e-5, y_c=yc)
     assert st["prequant_violations"] == 1
     assert abs(st["max_norm_prequant_err"] - 1e-3 / 7.9) < 1e-6
+
+
+# ------------------------------------------------------------------ weight side
+
+def test_weight_transform_undoes_the_activation_transform(oq):
+    # abstract: the inverse transform goes to the weights, so W' (T x) = W x.
+    rng = np.random.default_rng(21)
+    p = rand_params(4, 21)
+    w = rng.normal(size=(6, 128)).astype(np.float32)
+    x = rng.normal(size=(5, 128)).astype(np.float32)
+    wp = oq.weight_transform(w, p)
+    tx = oq.transform_dense(x, oq.expand(p))
+    lhs = tx @ wp.T
+    rhs = x.astype(np.float64) @ w.astype(np.float64).T
+    scale = np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T
+    assert np.all(np.abs(lhs - rhs) <= 1e-11 * np.maximum(scale, 1.0))
+
+
+def test_weight_transform_against_numpy_inverse(oq):
+    # an independent inverse (numpy.linalg.inv of the dense T_b) gives the same W'
+    rng = np.random.default_rng(22)
+    p = rand_params(3, 22)
+    w = rng.normal(size=(4, 96)).astype(np.float32)
+    T = oq.expand(p)
+    ref = np.concatenate([w[:, 32 * b:32 * b + 32].astype(np.float64) @ np.linalg.inv(T[b])
+                          for b in range(3)], axis=1)
+    np.testing.assert_allclose(oq.weight_transform(w, p), ref, rtol=1e-9, atol=1e-9)
+
+
+def test_weight_identity_and_encoding(oq):
+    rng = np.random.default_rng(23)
+    w = rng.normal(size=(8, 64)).astype(np.float32)
+    ident = synth.make_identity_params(2)
+    assert np.array_equal(oq.weight_transform(w, ident), w.astype(np.float64))
+    q, s, y = oq.quantize_weights(w, ident, want_y=True)
+    q2, s2 = oq.encode(w.astype(np.float64))
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)

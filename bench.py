@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--variant", choices=["butterfly", "mfma"], default="butterfly")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-sq", action="store_true", help="skip the SmoothQuant baseline")
+    ap.add_argument("--no-weights", action="store_true", help="skip the weight-side timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying a captured graph")
@@ -136,6 +137,41 @@ def cpu_baseline(x, p, seconds):
                       f"({el:.1f} s, fp64 dense 32x32 per block + MXFP4 encode)"}
 
 
+def weights_timing(args):
+    """The weight side (W T^-1 then MXFP4 along the input channels) on the FLUX MLP
+    up-projection W[12288, 3072] bf16, timed like the activation step over 4
+    rotating buffer sets (300 MB, beyond the last-level cache)."""
+    import torch
+
+    import synth
+    import online_activation_quantizer_amd as kq
+    cfg = synth.get_weight_config("flux_w_mlp")
+    sets = 4
+    w0, p0 = synth.make_weights(cfg)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+    ws = [torch.from_numpy(w0.view(np.int16)).cuda()]
+    for _ in range(1, sets):
+        ws.append((torch.randn((cfg.rows, cfg.d), generator=g, device="cuda") * cfg.std)
+                  .to(torch.bfloat16).view(torch.int16))
+    pd = torch.from_numpy(p0).cuda()
+    qs = [torch.empty((cfg.rows, cfg.d // 2), dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    ss = [torch.empty((cfg.rows, cfg.d // 32), dtype=torch.uint8, device="cuda") for _ in range(sets)]
+
+    def step(i):
+        j = i % sets
+        kq.kq_quantize_weights(ws[j], pd, q=qs[j], s=ss[j])
+
+    steps = max(8, args.steps // 4)
+    ms = (timed(step, steps, args.warmup, torch.cuda.current_stream()) if args.eager
+          else timed_graph(step, steps, args.warmup))
+    elems = cfg.rows * cfg.d
+    gbs = elems * BYTES_PER_ELEM / (ms * 1e-3) / 1e9
+    return {"workload": f"FLUX.1-schnell MLP up-projection weight {cfg.rows}x{cfg.d} bf16",
+            "ms_per_call": round(ms, 6), "gelem_s": round(elems / (ms * 1e-3) / 1e9, 3),
+            "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -189,6 +225,8 @@ def main():
         ms = timed_graph(kq_step, args.steps, args.warmup)
         sq_ms = None if args.no_sq else timed_graph(sq_step, args.steps, args.warmup)
 
+    weights = None if args.no_weights else weights_timing(args)
+
     # parity of one production step against the oracle
     parity = None
     try:
@@ -232,6 +270,8 @@ def main():
                               "t_sq_over_t_kq": round(sq_ms / ms, 4)}
         out["context"] = ("pages: on an MI350 the KroQuant quantizer kernel ran up to 14% faster "
                           "than a SmoothQuant kernel (shapes and timing method unstated)")
+    if weights is not None:
+        out["weights"] = weights
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -135,6 +135,28 @@ int sq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_
                        const float* mult, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
                        float* y, int64_t ldy, void* stream);
 
+/* Weight side (KroQuant abstract: the inverse of each block transform is folded
+ * into the weights, so a layer computes W' (T x) = W x).  For a weight matrix
+ * W[N][d] of a linear layer y = W x, row r becomes w'_r = w_r T^-1 per 32-channel
+ * block (w'_rb = T_b^-T w_rb as a column), and is encoded as MXFP4 along d with the
+ * same scale rule, codes and layout as kq_quantize (blocks of 32 input channels).
+ *   w       device [rows][ldw] of dtype; rows = N output channels; ldw in elements
+ *   params  device float32 [d/32][5][3], the same factors the activations use
+ *   q, s    as in kq_quantize
+ * The transform runs in fp32 from the factors: diag(1/d_i), then the lower shears
+ * by -u_k v_k, then the upper shears by -l_k (the mixed-product split of
+ * F^-T = L^-T U^-T).  Usually run once per learned transform, not per token.
+ * Errors: as sq_quantize. */
+int kq_quantize_weights(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
+                        const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                        void* stream);
+
+/* Validation entry of kq_quantize_weights: also writes the float32 W' (before
+ * quantization) into y [rows][ldy] (ldy >= d elements, 4-byte aligned). */
+int kq_weights_debug(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
+                     const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                     float* y, int64_t ldy, void* stream);
+
 /* Static text for a kq_status value (never NULL). */
 const char* kq_status_string(int status);
 

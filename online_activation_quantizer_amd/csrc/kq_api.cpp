@@ -134,6 +134,26 @@ int sq_impl(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, cons
   return e == hipSuccess ? KQ_OK : fail_hip(e);
 }
 
+int weights_impl(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
+                 const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, float* y,
+                 int64_t ldy, bool debug, void* stream) {
+  int rc = check_common(w, dtype, rows, d, ldw, params, q, ldq, s, lds);
+  if (rc != KQ_OK) return rc;
+  if (debug) {
+    if (ldy < d || ldy * 4 > kMaxPitch) return KQ_ERR_SHAPE;
+    if (rows > 0 && !y) return KQ_ERR_NULL;
+    if (rows > 0 && !aligned(y, 4)) return KQ_ERR_ALIGN;
+  }
+  if (rows == 0) return KQ_OK;
+  if (!aligned(params, 4)) return KQ_ERR_ALIGN;
+  kq::LaunchArgs a{w, dtype, rows, d, d / 32, ldw, params, q, ldq, s, lds, debug ? y : nullptr,
+                   ldy, stream, 0};
+  rc = current_cus(&a.cus);
+  if (rc != KQ_OK) return rc;
+  const hipError_t e = kq::launch_weights(a);
+  return e == hipSuccess ? KQ_OK : fail_hip(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -172,6 +192,18 @@ int sq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_
                        const float* mult, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
                        float* y, int64_t ldy, void* stream) {
   return sq_impl(x, dtype, rows, d, ldx, mult, q, ldq, s, lds, y, ldy, true, stream);
+}
+
+int kq_quantize_weights(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
+                        const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                        void* stream) {
+  return weights_impl(w, dtype, rows, d, ldw, params, q, ldq, s, lds, nullptr, 0, false, stream);
+}
+
+int kq_weights_debug(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
+                     const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                     float* y, int64_t ldy, void* stream) {
+  return weights_impl(w, dtype, rows, d, ldw, params, q, ldq, s, lds, y, ldy, true, stream);
 }
 
 const char* kq_status_string(int status) {

@@ -17,6 +17,13 @@
 // operations per element instead of 10 for the 2x2 butterfly and 64 for the
 // dense product, and everything stays in VGPRs.
 //
+// The same kernel folds the inverse into a weight matrix W[N][d] (KroQuant
+// abstract: the inverse transform goes to the weights).  Row r of W' = W T^-1 is
+// w'_b = T_b^-T w_b, and with F^-T = L^-T U^-T = S'(-l) L'(-u v) diag(1/u, u),
+// where S'(c) = [[1,c],[0,1]] and L'(c) = [[1,0],[c,1]], the same three Kronecker
+// products give: multiply by 1/d_i, lower shears x_q += (-u_k v_k) x_p, then upper
+// shears x_p += (-l_k) x_q.  Weight rows are quantized along d like activation rows.
+//
 // Lanes cover consecutive (row, block) units in memory order (a wave reads 4 KB
 // contiguous per row step) and advance through the rows with a stride that is a
 // multiple of nb, so every lane keeps one block for its whole life and computes
@@ -33,8 +40,8 @@ namespace {
 
 struct BlockConsts {
   float d[kBlk];
-  float su[5];  // u_k * v_k
-  float ll[5];  // l_k
+  float su[5];  // u_k * v_k   (negated for the weight side)
+  float ll[5];  // l_k         (negated for the weight side)
 };
 
 // The 15 factor parameters (l, u, v) x 5 of block b.
@@ -50,52 +57,73 @@ __device__ __forceinline__ BlockParams load_params(const float* __restrict__ par
   return r;
 }
 
-// The 42 constants of a block from its parameters.
+// The 42 constants of a block from its parameters.  INV builds those of T_b^-T:
+// the diagonal swaps u and 1/u, and both shear coefficients change sign.
+template <bool INV>
 __device__ __forceinline__ void make_consts(const BlockParams& bp, BlockConsts& c) {
-  float u[5], iu[5];
+  float d0[5], d1[5];  // the factor's diagonal entry for index bit 0 and bit 1
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
     const float l = bp.p[3 * k + 0], uk = bp.p[3 * k + 1], v = bp.p[3 * k + 2];
-    u[k] = uk;
-    iu[k] = __builtin_amdgcn_rcpf(uk);  // within 1 ulp; exact for powers of two
-    c.su[k] = uk * v;
-    c.ll[k] = l;
+    const float iu = __builtin_amdgcn_rcpf(uk);  // within 1 ulp; exact for powers of two
+    d0[k] = INV ? iu : uk;
+    d1[k] = INV ? uk : iu;
+    c.su[k] = INV ? -(uk * v) : uk * v;
+    c.ll[k] = INV ? -l : l;
   }
-  // d = [u1, 1/u1] (x) [u2, 1/u2] (x) ... (x) [u5, 1/u5], built from the right.
-  c.d[0] = u[4];
-  c.d[1] = iu[4];
+  // d = [d0_1, d1_1] (x) [d0_2, d1_2] (x) ... (x) [d0_5, d1_5], built from the right.
+  c.d[0] = d0[4];
+  c.d[1] = d1[4];
 #pragma unroll
   for (int k = 3, n = 2; k >= 0; --k, n *= 2) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i < n) {
-        c.d[n + i] = iu[k] * c.d[i];
-        c.d[i] = u[k] * c.d[i];
+        c.d[n + i] = d1[k] * c.d[i];
+        c.d[i] = d0[k] * c.d[i];
       }
     }
   }
 }
 
-__device__ __forceinline__ void transform(float (&v)[kBlk], const BlockConsts& c) {
-#pragma unroll
-  for (int i = 0; i < kBlk; ++i) v[i] *= c.d[i];
-#pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    const int st = 16 >> k;
-#pragma unroll
-    for (int i = 0; i < kBlk; ++i)
-      if (!(i & st)) v[i] = __builtin_fmaf(c.su[k], v[i + st], v[i]);
-  }
+// x_p += coef_k x_q over the pairs p < q that differ in index bit 4-k.
+__device__ __forceinline__ void upper_shears(float (&v)[kBlk], const float (&coef)[5]) {
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
     const int st = 16 >> k;
 #pragma unroll
     for (int i = 0; i < kBlk; ++i)
-      if (!(i & st)) v[i + st] = __builtin_fmaf(c.ll[k], v[i], v[i + st]);
+      if (!(i & st)) v[i] = __builtin_fmaf(coef[k], v[i + st], v[i]);
   }
 }
 
-template <int DT, bool WRITE_Y>
+// x_q += coef_k x_p over the same pairs.
+__device__ __forceinline__ void lower_shears(float (&v)[kBlk], const float (&coef)[5]) {
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int st = 16 >> k;
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i)
+      if (!(i & st)) v[i + st] = __builtin_fmaf(coef[k], v[i], v[i + st]);
+  }
+}
+
+// T_b x (upper shears by u v, then lower by l) or, for INV, T_b^-T x (lower shears
+// by -u v, then upper by -l), after the diagonal.
+template <bool INV>
+__device__ __forceinline__ void transform(float (&v)[kBlk], const BlockConsts& c) {
+#pragma unroll
+  for (int i = 0; i < kBlk; ++i) v[i] *= c.d[i];
+  if (INV) {
+    lower_shears(v, c.su);
+    upper_shears(v, c.ll);
+  } else {
+    upper_shears(v, c.su);
+    lower_shears(v, c.ll);
+  }
+}
+
+template <int DT, bool WRITE_Y, bool INV>
 __global__ __launch_bounds__(kThreads) void butterfly_kernel(
     const uint8_t* __restrict__ x, uint32_t rows, uint32_t nb, uint32_t ldx, uint32_t tstep,
     const float* __restrict__ params, uint8_t* __restrict__ q, uint32_t ldq,
@@ -115,31 +143,37 @@ __global__ __launch_bounds__(kThreads) void butterfly_kernel(
   uint8_t* const ycol = reinterpret_cast<uint8_t*>(y) + b * kBlk * 4;
   for_each_row<DT, kRowDepth>(
       x + (size_t)b * kBlk * (DT == DT_BF16 ? 2 : 4), rows, ldx, t, tstep,
-      [&] { make_consts(bp, c); },
+      [&] { make_consts<INV>(bp, c); },
       [&](float (&v)[kBlk], uint32_t r) {
-        transform(v, c);
+        transform<INV>(v, c);
         if (WRITE_Y) store_y(reinterpret_cast<float*>(ycol + (uint64_t)r * ldy), v);
         encode_store(v, qcol + (uint64_t)r * ldq, scol + (uint64_t)r * lds);
       });
 }
 
-template <int DT, bool WRITE_Y>
+template <int DT, bool WRITE_Y, bool INV>
 hipError_t launch_t(const LaunchArgs& a) {
   uint32_t tstep = 0;
   const int64_t grid = grid_for_units(a.rows, a.nb, a.cus, kBlocksPerCU, &tstep);
   const int64_t esz = DT == DT_BF16 ? 2 : 4;
-  hipLaunchKernelGGL((butterfly_kernel<DT, WRITE_Y>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((butterfly_kernel<DT, WRITE_Y, INV>), dim3((unsigned)grid), dim3(kThreads), 0,
                      (hipStream_t)a.stream, (const uint8_t*)a.x, (uint32_t)a.rows,
                      (uint32_t)a.nb, (uint32_t)(a.ldx * esz), tstep, (const float*)a.t, a.q,
                      (uint32_t)a.ldq, a.s, (uint32_t)a.lds, a.y, (uint32_t)(a.ldy * 4));
   return hipGetLastError();
 }
 
+template <bool INV>
+hipError_t launch_dir(const LaunchArgs& a) {
+  if (a.dtype == DT_BF16)
+    return a.y ? launch_t<DT_BF16, true, INV>(a) : launch_t<DT_BF16, false, INV>(a);
+  return a.y ? launch_t<DT_FP32, true, INV>(a) : launch_t<DT_FP32, false, INV>(a);
+}
+
 }  // namespace
 
-hipError_t launch_butterfly(const LaunchArgs& a) {
-  if (a.dtype == DT_BF16) return a.y ? launch_t<DT_BF16, true>(a) : launch_t<DT_BF16, false>(a);
-  return a.y ? launch_t<DT_FP32, true>(a) : launch_t<DT_FP32, false>(a);
-}
+hipError_t launch_butterfly(const LaunchArgs& a) { return launch_dir<false>(a); }
+
+hipError_t launch_weights(const LaunchArgs& a) { return launch_dir<true>(a); }
 
 }  // namespace kq

@@ -22,7 +22,8 @@ KQ_T_PARAMS, KQ_T_DENSE_F32, KQ_T_DENSE_BF16X3 = 0, 1, 2
 KQ_AUTO, KQ_BUTTERFLY, KQ_MFMA = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
-                    "sq_transform_debug", "kq_status_string", "kq_last_hip_error")
+                    "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug",
+                    "kq_status_string", "kq_last_hip_error")
 
 
 class KQError(RuntimeError):
@@ -50,6 +51,8 @@ def lib():
         L.sq_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P]
         L.kq_transform_debug.argtypes = [P, I, I64, I64, I64, P, I, P, I64, P, I64, I, P, I64, P]
         L.sq_transform_debug.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I64, P]
+        L.kq_quantize_weights.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P]
+        L.kq_weights_debug.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I64, P]
         L.kq_status_string.argtypes = [I]
         L.kq_status_string.restype = ctypes.c_char_p
         L.kq_last_hip_error.argtypes = []
@@ -161,4 +164,27 @@ def sq_transform_debug(x, mult, q=None, s=None, y=None, stream=None):
                                     q.data_ptr(), _row_pitch(q), s.data_ptr(), _row_pitch(s),
                                     y.data_ptr(), _row_pitch(y), _stream(stream)),
            "sq_transform_debug")
+    return q, s, y
+
+
+def kq_quantize_weights(w, params, q=None, s=None, stream=None):
+    """MXFP4 (q [N, d/2], s [N, d/32]) of W T^-1 for weights w [N, d] (blocks along d)."""
+    q, s = _outputs(w, q, s)
+    rows, d = w.shape
+    _check(lib().kq_quantize_weights(w.data_ptr(), _dtype_code(w), rows, d, _row_pitch(w),
+                                     params.data_ptr(), q.data_ptr(), _row_pitch(q), s.data_ptr(),
+                                     _row_pitch(s), _stream(stream)), "kq_quantize_weights")
+    return q, s
+
+
+def kq_weights_debug(w, params, q=None, s=None, y=None, stream=None):
+    """kq_quantize_weights that also returns the float32 W T^-1 [N, d]."""
+    import torch
+    q, s = _outputs(w, q, s)
+    rows, d = w.shape
+    if y is None:
+        y = torch.empty((rows, d), dtype=torch.float32, device=w.device)
+    _check(lib().kq_weights_debug(w.data_ptr(), _dtype_code(w), rows, d, _row_pitch(w), params.data_ptr(),
+                                  q.data_ptr(), _row_pitch(q), s.data_ptr(), _row_pitch(s),
+                                  y.data_ptr(), _row_pitch(y), _stream(stream)), "kq_weights_debug")
     return q, s, y

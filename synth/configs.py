@@ -70,3 +70,36 @@ def sweep_call(i: int) -> Config:
 
 def get_config(name: str) -> Config:
     return CONFIGS[name]
+
+
+@dataclass(frozen=True)
+class WeightConfig:
+    """A linear layer's weight W[rows = output channels][d = input channels]; the
+    quantizer's blocks run along d, matching the activations that layer takes."""
+    name: str
+    rows: int
+    d: int
+    dtype: str
+    std: float              # base standard deviation of the entries
+    row_spread: float       # per-output-row std multiplier exp(N(0, row_spread))
+    seed: int
+
+    @property
+    def nb(self) -> int:
+        return self.d // 32
+
+
+WEIGHT_CONFIGS = {
+    # small fp32 case for the oracle
+    "tiny_w": WeightConfig("tiny_w", 192, 1152, "fp32", 0.02, 0.3, seed=20),
+    # PixArt-Sigma attention projection 1152 -> 1152
+    "pixart_w": WeightConfig("pixart_w", 1152, 1152, "bf16", 0.02, 0.3, seed=21),
+    # FLUX.1-schnell joint-stream MLP up-projection 3072 -> 12288 (input width 3072)
+    "flux_w_mlp": WeightConfig("flux_w_mlp", 12288, 3072, "bf16", 0.02, 0.3, seed=22),
+    # FLUX.1-schnell MLP down-projection 12288 -> 3072 (input width 12288)
+    "flux_w_down": WeightConfig("flux_w_down", 3072, 12288, "bf16", 0.01, 0.3, seed=23),
+}
+
+
+def get_weight_config(name: str) -> WeightConfig:
+    return WEIGHT_CONFIGS[name]

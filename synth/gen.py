@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .configs import Config
+from .configs import Config, WeightConfig
 
 
 def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
@@ -94,3 +94,16 @@ def make_activations_device(cfg: Config, seed: int, device="cuda"):
     out_ch = torch.randperm(d, generator=g, device=device)[: cfg.n_outliers]
     x[:, out_ch] *= cfg.outlier_scale
     return x.to(torch.bfloat16) if cfg.dtype == "bf16" else x
+
+
+def make_weights(cfg: WeightConfig, seed: int | None = None):
+    """(w, params): weights W[rows, d] (uint16 bf16 bits or float32) drawn as
+    N(0, std * exp(N(0, row_spread))) per output row, then the factor parameters of
+    the d/32 input blocks, from one seeded stream."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    rs = np.exp(rng.normal(0.0, cfg.row_spread, size=(cfg.rows, 1))).astype(np.float32)
+    w = rng.standard_normal(size=(cfg.rows, cfg.d), dtype=np.float32) * np.float32(cfg.std) * rs
+    params = make_params(cfg.nb, rng)
+    if cfg.dtype == "bf16":
+        return bf16_bits_from_f32(w), params
+    return np.ascontiguousarray(w, np.float32), params

@@ -27,7 +27,8 @@ def header_functions():
 def test_header_symbols_exported(L):
     names = header_functions()
     assert {"kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
-            "sq_transform_debug", "kq_status_string", "kq_last_hip_error"} <= set(names)
+            "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug", "kq_status_string",
+            "kq_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -85,6 +86,17 @@ def test_sq_and_debug_validation(L):
     assert L.kq_transform_debug(X, 0, 4, 64, 64, T, 0, Q, 32, S, 2, 0, Y, 32, None) == SHAPE
     assert L.kq_transform_debug(X, 0, 4, 64, 64, T, 0, Q, 32, S, 2, 0, Y + 2, 64, None) == ALIGN
     assert L.sq_transform_debug(X, 0, 4, 64, 64, T, Q, 32, S, 2, None, 64, None) == NULL
+
+
+def test_weights_validation(L):
+    assert L.kq_quantize_weights(X, 0, 4, 64, 64, None, Q, 32, S, 2, None) == NULL
+    assert L.kq_quantize_weights(X, 0, 4, 64, 64, T + 2, Q, 32, S, 2, None) == ALIGN
+    assert L.kq_quantize_weights(X, 5, 4, 64, 64, T, Q, 32, S, 2, None) == DTYPE
+    assert L.kq_quantize_weights(X, 0, 4, 48, 48, T, Q, 24, S, 2, None) == SHAPE
+    assert L.kq_quantize_weights(X + 8, 0, 4, 64, 64, T, Q, 32, S, 2, None) == ALIGN
+    assert L.kq_quantize_weights(None, 0, 0, 64, 64, None, None, 32, None, 2, None) == OK
+    assert L.kq_weights_debug(X, 0, 4, 64, 64, T, Q, 32, S, 2, None, 64, None) == NULL
+    assert L.kq_weights_debug(X, 0, 4, 64, 64, T, Q, 32, S, 2, Y, 32, None) == SHAPE
 
 
 def test_expand_validation(L):

@@ -44,3 +44,15 @@ def test_factor_distribution():
     p = synth.make_params(20000, np.random.default_rng(0))
     assert abs(p[..., 0].std() - 0.5) < 0.01 and abs(p[..., 2].std() - 0.5) < 0.01
     assert abs(np.log(p[..., 1]).std() - 0.3) < 0.01
+
+
+def test_weights_seeded_and_shaped():
+    cfg = synth.get_weight_config("tiny_w")
+    w1, p1 = synth.make_weights(cfg)
+    w2, p2 = synth.make_weights(cfg)
+    assert w1.shape == (cfg.rows, cfg.d) and w1.dtype == np.float32
+    assert p1.shape == (cfg.nb, 5, 3)
+    assert np.array_equal(w1, w2) and np.array_equal(p1, p2)
+    assert 0.01 < float(np.std(w1)) < 0.04
+    wb, _ = synth.make_weights(synth.get_weight_config("pixart_w"))
+    assert wb.dtype == np.uint16

@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-sq", action="store_true", help="skip the SmoothQuant baseline")
     ap.add_argument("--no-weights", action="store_true", help="skip the weight-side timing")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the same-bytes streaming kernel (practical HBM ceiling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying a captured graph")
@@ -137,6 +139,28 @@ def cpu_baseline(x, p, seconds):
                       f"({el:.1f} s, fp64 dense 32x32 per block + MXFP4 encode)"}
 
 
+def stream_ceiling(args, xs, qs, ss, kq_ms):
+    """The same bytes per call (64 B read, 17 B written per 32-element unit) moved by
+    a kernel with no arithmetic, timed like the quantizer step over the same buffer
+    pool at a few grid sizes; the fastest is the practical ceiling at this size."""
+    from online_activation_quantizer_amd import bench_stream
+    P = len(xs)
+    best = None
+    for grid in (768, 1024, 1536, 2048, 3072):
+        def step(i, grid=grid):
+            j = i % P
+            bench_stream.kq_bench_stream(xs[j], qs[j], ss[j], grid)
+        ms = (timed(step, args.steps, args.warmup, __import__("torch").cuda.current_stream())
+              if args.eager else timed_graph(step, args.steps, args.warmup))
+        if best is None or ms < best[0]:
+            best = (ms, grid)
+    ms, grid = best
+    elems = xs[0].numel()
+    gbs = elems * BYTES_PER_ELEM / (ms * 1e-3) / 1e9
+    return {"ms_per_step": round(ms, 6), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "grid": grid, "kq_time_over_ceiling_time": round(kq_ms / ms, 4)}
+
+
 def weights_timing(args):
     """The weight side (W T^-1 then MXFP4 along the input channels) on the FLUX MLP
     up-projection W[12288, 3072] bf16, timed like the activation step over 4
@@ -226,6 +250,7 @@ def main():
         sq_ms = None if args.no_sq else timed_graph(sq_step, args.steps, args.warmup)
 
     weights = None if args.no_weights else weights_timing(args)
+    ceiling = None if args.no_ceiling else stream_ceiling(args, xs, qs, ss, ms)
 
     # parity of one production step against the oracle
     parity = None
@@ -270,6 +295,8 @@ def main():
                               "t_sq_over_t_kq": round(sq_ms / ms, 4)}
         out["context"] = ("pages: on an MI350 the KroQuant quantizer kernel ran up to 14% faster "
                           "than a SmoothQuant kernel (shapes and timing method unstated)")
+    if ceiling is not None:
+        out["stream_ceiling"] = ceiling
     if weights is not None:
         out["weights"] = weights
     if args.calib_copy_mib > 0:

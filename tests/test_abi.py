@@ -18,8 +18,8 @@ def L():
     return kq.lib()
 
 
-def header_functions():
-    text = open(os.path.join(ROOT, "include", "kq.h")).read()
+def header_functions(name="kq.h"):
+    text = open(os.path.join(ROOT, "include", name)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
@@ -31,6 +31,26 @@ def test_header_symbols_exported(L):
             "kq_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_every_header_is_covered():
+    # each public header belongs to one of the two libraries checked here
+    assert sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")) == \
+        ["kq.h", "kq_bench.h"]
+
+
+def test_bench_helper_library(L):
+    from online_activation_quantizer_amd import bench_stream
+    B = bench_stream.lib()
+    names = header_functions("kq_bench.h")
+    assert names == ["kq_bench_stream"]
+    for n in names:
+        assert hasattr(B, n), n
+    assert B.kq_bench_stream(X, 4, Q, S, 0, None) == SHAPE
+    assert B.kq_bench_stream(X, -1, Q, S, 8, None) == SHAPE
+    assert B.kq_bench_stream(None, 4, Q, S, 8, None) == NULL
+    assert B.kq_bench_stream(X + 4, 4, Q, S, 8, None) == ALIGN
+    assert B.kq_bench_stream(None, 0, None, None, 8, None) == OK
 
 
 def test_oracle_not_linked_into_product(L):

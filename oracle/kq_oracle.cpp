@@ -279,6 +279,37 @@ int oq_sq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ld
   return rc;
 }
 
+int oq_hadamard_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                         uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, double* y_out,
+                         int nthreads) {
+  if (!x || !q || !s || bad_shape(rows, d, ldx) || (dtype != OQ_BF16 && dtype != OQ_FP32) ||
+      ldq < d / 2 || lds < d / kBlk)
+    return -1;
+  // the Sylvester matrix by its closed form, scaled to be orthonormal
+  double H[kBlk][kBlk];
+  const double norm = 1.0 / std::sqrt((double)kBlk);
+  for (int i = 0; i < kBlk; ++i)
+    for (int j = 0; j < kBlk; ++j) H[i][j] = (__builtin_popcount(i & j) & 1) ? -norm : norm;
+  int rc = 0;
+  parallel_rows(rows, nthreads, [&](int64_t r0, int64_t r1) {
+    const int64_t n = r1 - r0;
+    std::vector<double> ybuf;
+    double* y = y_out ? y_out + r0 * d : (ybuf.resize((size_t)n * d), ybuf.data());
+    for (int64_t t = 0; t < n; ++t)
+      for (int64_t b = 0; b < d / kBlk; ++b) {
+        double xb[kBlk];
+        for (int j = 0; j < kBlk; ++j) xb[j] = oq_load(x, dtype, (r0 + t) * ldx + b * kBlk + j);
+        for (int i = 0; i < kBlk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < kBlk; ++j) acc += H[i][j] * xb[j];
+          y[t * d + b * kBlk + i] = acc;
+        }
+      }
+    if (oq_encode(y, n, d, q + r0 * ldq, ldq, s + r0 * lds, lds) != 0) rc = -1;
+  });
+  return rc;
+}
+
 int oq_weight_transform(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
                         const float* params, double* w_out) {
   if (rows == 0 && !bad_shape(rows, d, ldw)) return 0;

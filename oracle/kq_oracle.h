@@ -111,6 +111,14 @@ int oq_quantize_weights(const void* w, int dtype, int64_t rows, int64_t d, int64
                         const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
                         double* w_out, int nthreads);
 
+/* Fixed block-Hadamard comparison transform: y_b = H x_b / sqrt(32) with the
+ * Sylvester matrix H[i][j] = (-1)^popcount(i & j) (symmetric, H H = 32 I, so the
+ * weights take the same transform), then the MXFP4 encoding.  [ABS] (fixed
+ * Hadamard transforms are the accurate but costly comparison point) */
+int oq_hadamard_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                         uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, double* y_out,
+                         int nthreads);
+
 /* Parity accounting of candidate outputs against the oracle's fp64 values y_o.
  * Per block the tolerance is tol_coef * max|x_blk| (tol_mode 0, the fp32 rule) or
  * tol_coef * max|y_o_blk| (tol_mode 1, the block-relative bf16 rule).

@@ -58,6 +58,7 @@ def lib():
         L.oq_encode.argtypes = [P, I64, I64, P, I64, P, I64]
         L.oq_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
         L.oq_sq_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
+        L.oq_hadamard_quantize.argtypes = [P, I, I64, I64, I64, P, I64, P, I64, P, I]
         L.oq_weight_transform.argtypes = [P, I, I64, I64, I64, P, P]
         L.oq_quantize_weights.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
         L.oq_classify.argtypes = [P, I, I64, I64, I64, P, I, D, P, I64, P, I64, P, I64, P]
@@ -186,6 +187,19 @@ def sq_quantize(x: np.ndarray, mult: np.ndarray, want_y: bool = False, nthreads:
     rc = lib().oq_sq_quantize(_ptr(x), dt, rows, d, ldx, _ptr(m), _ptr(q), d // 2, _ptr(s), d // 32,
                               _ptr(y) if want_y else None, nthreads)
     _check(rc, "sq_quantize")
+    return q, s, y
+
+
+def hadamard_quantize(x: np.ndarray, want_y: bool = False, nthreads: int = 0):
+    """(q, s, y fp64 or None) of the fixed block-Hadamard comparison transform."""
+    dt, rows, ldx = _x_info(x)
+    d = x.shape[1]
+    q = np.zeros((rows, d // 2), np.uint8)
+    s = np.zeros((rows, d // 32), np.uint8)
+    y = np.zeros((rows, d), np.float64) if want_y else None
+    rc = lib().oq_hadamard_quantize(_ptr(x), dt, rows, d, ldx, _ptr(q), d // 2, _ptr(s), d // 32,
+                                    _ptr(y) if want_y else None, nthreads)
+    _check(rc, "hadamard_quantize")
     return q, s, y
 
 

@@ -55,6 +55,9 @@ MUTANTS = {
     "weight_side_transposed": (
         "for (int i = 0; i < kBlk; ++i) acc += wb[i] * Tb[i * kBlk + j];",
         "for (int i = 0; i < kBlk; ++i) acc += wb[i] * Tb[j * kBlk + i];"),
+    "hadamard_wrong_sign_rule": (
+        "H[i][j] = (__builtin_popcount(i & j) & 1) ? -norm : norm;",
+        "H[i][j] = (__builtin_popcount(i | j) & 1) ? -norm : norm;"),
     "amax_without_abs": (
         "        amax = std::max(amax, std::fabs(yb[i]));\n      }\n      uint8_t* qb",
         "        amax = std::max(amax, yb[i]);\n      }\n      uint8_t* qb"),

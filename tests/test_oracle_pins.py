@@ -323,3 +323,45 @@ def test_weight_identity_and_encoding(oq):
     q, s, y = oq.quantize_weights(w, ident, want_y=True)
     q2, s2 = oq.encode(w.astype(np.float64))
     assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+# ------------------------------------------------------------------ fixed Hadamard comparison
+
+def test_hadamard_columns_match_scipy(oq):
+    # unit inputs read the transform's columns; scipy builds the Sylvester matrix independently
+    from scipy.linalg import hadamard
+    x = np.zeros((32, 64), np.float32)
+    for j in range(32):
+        x[j, j] = 1.0
+        x[j, 32 + j] = -2.0
+    _, _, y = oq.hadamard_quantize(x, want_y=True)
+    H = hadamard(32) / np.sqrt(32.0)
+    np.testing.assert_allclose(y[:, :32], H.T, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(y[:, 32:], -2.0 * H.T, rtol=0, atol=1e-15)
+
+
+def test_hadamard_is_an_orthonormal_involution(oq):
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(41)
+    x = rng.normal(size=(16, 96)).astype(np.float32)
+    _, _, y = oq.hadamard_quantize(x, want_y=True)
+    xb, yb = x.astype(np.float64).reshape(16, 3, 32), y.reshape(16, 3, 32)
+    np.testing.assert_allclose(np.sum(yb ** 2, -1), np.sum(xb ** 2, -1), rtol=1e-13)  # Parseval
+    # applying it again returns the input (H / sqrt(32) is symmetric and orthogonal)
+    y32 = y.astype(np.float32)
+    _, _, z = oq.hadamard_quantize(y32, want_y=True)
+    H = hadamard(32) / np.sqrt(32.0)
+    ref = (y32.astype(np.float64).reshape(16, 3, 32) @ H.T).reshape(16, 96)
+    np.testing.assert_allclose(z, ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(z, x.astype(np.float64), rtol=0, atol=1e-6 * np.abs(x).max())
+
+
+def test_hadamard_constant_block_and_encoding(oq):
+    # a constant block concentrates on channel 0: sqrt(32) * c, the rest 0
+    x = np.full((2, 32), 0.75, np.float32)
+    q, s, y = oq.hadamard_quantize(x, want_y=True)
+    expect = np.zeros(32)
+    expect[0] = np.sqrt(32.0) * 0.75
+    np.testing.assert_allclose(y[0], expect, atol=1e-15)
+    q2, s2 = oq.encode(y)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)

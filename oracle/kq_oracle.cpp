@@ -285,11 +285,13 @@ int oq_hadamard_quantize(const void* x, int dtype, int64_t rows, int64_t d, int6
   if (!x || !q || !s || bad_shape(rows, d, ldx) || (dtype != OQ_BF16 && dtype != OQ_FP32) ||
       ldq < d / 2 || lds < d / kBlk)
     return -1;
-  // the Sylvester matrix by its closed form, scaled to be orthonormal
+  // the Sylvester matrix by its closed form (entries +-1); the 1/sqrt(32) scale is
+  // applied to the finished sum, so an exact cancellation stays +0 as in exact
+  // arithmetic (the sign of zero decides a code bit)
   double H[kBlk][kBlk];
   const double norm = 1.0 / std::sqrt((double)kBlk);
   for (int i = 0; i < kBlk; ++i)
-    for (int j = 0; j < kBlk; ++j) H[i][j] = (__builtin_popcount(i & j) & 1) ? -norm : norm;
+    for (int j = 0; j < kBlk; ++j) H[i][j] = (__builtin_popcount(i & j) & 1) ? -1.0 : 1.0;
   int rc = 0;
   parallel_rows(rows, nthreads, [&](int64_t r0, int64_t r1) {
     const int64_t n = r1 - r0;
@@ -302,7 +304,7 @@ int oq_hadamard_quantize(const void* x, int dtype, int64_t rows, int64_t d, int6
         for (int i = 0; i < kBlk; ++i) {
           double acc = 0.0;
           for (int j = 0; j < kBlk; ++j) acc += H[i][j] * xb[j];
-          y[t * d + b * kBlk + i] = acc;
+          y[t * d + b * kBlk + i] = acc * norm;
         }
       }
     if (oq_encode(y, n, d, q + r0 * ldq, ldq, s + r0 * lds, lds) != 0) rc = -1;

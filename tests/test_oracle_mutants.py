@@ -56,8 +56,11 @@ MUTANTS = {
         "for (int i = 0; i < kBlk; ++i) acc += wb[i] * Tb[i * kBlk + j];",
         "for (int i = 0; i < kBlk; ++i) acc += wb[i] * Tb[j * kBlk + i];"),
     "hadamard_wrong_sign_rule": (
-        "H[i][j] = (__builtin_popcount(i & j) & 1) ? -norm : norm;",
-        "H[i][j] = (__builtin_popcount(i | j) & 1) ? -norm : norm;"),
+        "H[i][j] = (__builtin_popcount(i & j) & 1) ? -1.0 : 1.0;",
+        "H[i][j] = (__builtin_popcount(i | j) & 1) ? -1.0 : 1.0;"),
+    "hadamard_scale_dropped": (
+        "y[t * d + b * kBlk + i] = acc * norm;",
+        "y[t * d + b * kBlk + i] = acc;"),
     "amax_without_abs": (
         "        amax = std::max(amax, std::fabs(yb[i]));\n      }\n      uint8_t* qb",
         "        amax = std::max(amax, yb[i]);\n      }\n      uint8_t* qb"),

@@ -365,3 +365,13 @@ def test_hadamard_constant_block_and_encoding(oq):
     np.testing.assert_allclose(y[0], expect, atol=1e-15)
     q2, s2 = oq.encode(y)
     assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+def test_hadamard_exact_cancellation_is_positive_zero(oq):
+    # x = (1, 1, 0, ...): every odd-indexed coefficient is (1 - 1)/sqrt(32) = 0 exactly, a
+    # +0 in exact arithmetic, so its code is 0x0 (a negative zero would encode 0x8)
+    x = np.zeros((1, 32), np.float32)
+    x[0, :2] = 1.0
+    q, s, y = oq.hadamard_quantize(x, want_y=True)
+    assert np.all(y[0, 1::2] == 0.0) and not np.any(np.signbit(y[0, 1::2]))
+    assert np.all((q[0] >> 4) == 0)  # odd channels sit in the high nibbles

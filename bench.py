@@ -36,7 +36,8 @@ def parse():
     ap.add_argument("--pool", type=int, default=16, help="distinct buffer sets rotated over")
     ap.add_argument("--variant", choices=["butterfly", "mfma"], default="butterfly")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--no-sq", action="store_true", help="skip the SmoothQuant baseline")
+    ap.add_argument("--no-sq", action="store_true",
+                    help="skip the SmoothQuant and block-Hadamard comparison timings")
     ap.add_argument("--no-weights", action="store_true", help="skip the weight-side timing")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the same-bytes streaming kernel (practical HBM ceiling)")
@@ -242,12 +243,18 @@ def main():
         j = i % P
         kq.sq_quantize(xs[j], m_dev, q=qs[j], s=ss[j])
 
+    def hq_step(i):
+        j = i % P
+        kq.hq_quantize(xs[j], q=qs[j], s=ss[j])
+
     if args.eager:
         ms = timed(kq_step, args.steps, args.warmup, stream)
         sq_ms = None if args.no_sq else timed(sq_step, args.steps, args.warmup, stream)
+        hq_ms = None if args.no_sq else timed(hq_step, args.steps, args.warmup, stream)
     else:
         ms = timed_graph(kq_step, args.steps, args.warmup)
         sq_ms = None if args.no_sq else timed_graph(sq_step, args.steps, args.warmup)
+        hq_ms = None if args.no_sq else timed_graph(hq_step, args.steps, args.warmup)
 
     weights = None if args.no_weights else weights_timing(args)
     ceiling = None if args.no_ceiling else stream_ceiling(args, xs, qs, ss, ms)
@@ -293,6 +300,9 @@ def main():
         sq_gbs = elems * BYTES_PER_ELEM / (sq_ms * 1e-3) / 1e9
         out["sq_baseline"] = {"ms_per_step": round(sq_ms, 6), "gbs": round(sq_gbs, 1),
                               "t_sq_over_t_kq": round(sq_ms / ms, 4)}
+        hq_gbs = elems * BYTES_PER_ELEM / (hq_ms * 1e-3) / 1e9
+        out["hadamard_baseline"] = {"ms_per_step": round(hq_ms, 6), "gbs": round(hq_gbs, 1),
+                                    "t_hq_over_t_kq": round(hq_ms / ms, 4)}
         out["context"] = ("pages: on an MI350 the KroQuant quantizer kernel ran up to 14% faster "
                           "than a SmoothQuant kernel (shapes and timing method unstated)")
     if ceiling is not None:

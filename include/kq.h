@@ -157,6 +157,23 @@ int kq_weights_debug(const void* w, int dtype, int64_t rows, int64_t d, int64_t 
                      const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
                      float* y, int64_t ldy, void* stream);
 
+/* Fixed block-Hadamard comparison transform (KroQuant abstract: fixed Hadamard
+ * rotations quantize well but are the costly alternative at large blocks): here
+ * at the same 32-channel blocks, y_b = H x_b / sqrt(32) with the Sylvester matrix
+ * H[i][j] = (-1)^popcount(i & j), then the same MXFP4 encoding and layout as
+ * kq_quantize.  H / sqrt(32) is symmetric and orthogonal, so a layer's weights
+ * take this same call.  Computed in fp32: five add/subtract stages, then one
+ * multiply by fp32(1/sqrt(32)).
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_DTYPE, KQ_ERR_HIP. */
+int hq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, uint8_t* q,
+                int64_t ldq, uint8_t* s, int64_t lds, void* stream);
+
+/* Validation entry of hq_quantize: also writes the float32 transformed values
+ * into y [rows][ldy] (ldy >= d elements, 4-byte aligned). */
+int hq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                       uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, float* y, int64_t ldy,
+                       void* stream);
+
 /* Static text for a kq_status value (never NULL). */
 const char* kq_status_string(int status);
 

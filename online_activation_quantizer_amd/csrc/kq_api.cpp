@@ -154,6 +154,26 @@ int weights_impl(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
   return e == hipSuccess ? KQ_OK : fail_hip(e);
 }
 
+int hadamard_impl(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, uint8_t* q,
+                  int64_t ldq, uint8_t* s, int64_t lds, float* y, int64_t ldy, bool debug,
+                  void* stream) {
+  // the transform takes no operand: any non-null stand-in passes the shared check
+  int rc = check_common(x, dtype, rows, d, ldx, q, q, ldq, s, lds);
+  if (rc != KQ_OK) return rc;
+  if (debug) {
+    if (ldy < d || ldy * 4 > kMaxPitch) return KQ_ERR_SHAPE;
+    if (rows > 0 && !y) return KQ_ERR_NULL;
+    if (rows > 0 && !aligned(y, 4)) return KQ_ERR_ALIGN;
+  }
+  if (rows == 0) return KQ_OK;
+  kq::LaunchArgs a{x, dtype, rows, d, d / 32, ldx, nullptr, q, ldq, s, lds, debug ? y : nullptr,
+                   ldy, stream, 0};
+  rc = current_cus(&a.cus);
+  if (rc != KQ_OK) return rc;
+  const hipError_t e = kq::launch_hadamard(a);
+  return e == hipSuccess ? KQ_OK : fail_hip(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -204,6 +224,17 @@ int kq_weights_debug(const void* w, int dtype, int64_t rows, int64_t d, int64_t 
                      const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
                      float* y, int64_t ldy, void* stream) {
   return weights_impl(w, dtype, rows, d, ldw, params, q, ldq, s, lds, y, ldy, true, stream);
+}
+
+int hq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, uint8_t* q,
+                int64_t ldq, uint8_t* s, int64_t lds, void* stream) {
+  return hadamard_impl(x, dtype, rows, d, ldx, q, ldq, s, lds, nullptr, 0, false, stream);
+}
+
+int hq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                       uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, float* y, int64_t ldy,
+                       void* stream) {
+  return hadamard_impl(x, dtype, rows, d, ldx, q, ldq, s, lds, y, ldy, true, stream);
 }
 
 const char* kq_status_string(int status) {

@@ -24,6 +24,12 @@
 // products give: multiply by 1/d_i, lower shears x_q += (-u_k v_k) x_p, then upper
 // shears x_p += (-l_k) x_q.  Weight rows are quantized along d like activation rows.
 //
+// A third mode runs the fixed block-Hadamard comparison transform (KroQuant
+// abstract: fixed Hadamard rotations are the accurate but costly alternative):
+// five add/subtract stages (a, b) -> (a + b, a - b) over the same index pairs, then
+// a multiply by fp32(1/sqrt(32)).  H/sqrt(32) is symmetric and orthogonal, so
+// weights take the same transform.
+//
 // Lanes cover consecutive (row, block) units in memory order (a wave reads 4 KB
 // contiguous per row step) and advance through the rows with a stride that is a
 // multiple of nb, so every lane keeps one block for its whole life and computes
@@ -108,6 +114,25 @@ __device__ __forceinline__ void lower_shears(float (&v)[kBlk], const float (&coe
   }
 }
 
+enum : int { kForward = 0, kWeights = 1, kHadamard = 2 };
+
+// (a, b) -> (a + b, a - b) over the pairs of every index bit, then 1/sqrt(32).
+__device__ __forceinline__ void hadamard(float (&v)[kBlk]) {
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int st = 16 >> k;
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i)
+      if (!(i & st)) {
+        const float a = v[i], b = v[i + st];
+        v[i] = a + b;
+        v[i + st] = a - b;
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < kBlk; ++i) v[i] *= 0.17677669529663687f;  // fp32(1/sqrt(32))
+}
+
 // T_b x (upper shears by u v, then lower by l) or, for INV, T_b^-T x (lower shears
 // by -u v, then upper by -l), after the diagonal.
 template <bool INV>
@@ -123,7 +148,7 @@ __device__ __forceinline__ void transform(float (&v)[kBlk], const BlockConsts& c
   }
 }
 
-template <int DT, bool WRITE_Y, bool INV>
+template <int DT, bool WRITE_Y, int MODE>
 __global__ __launch_bounds__(kThreads) void butterfly_kernel(
     const uint8_t* __restrict__ x, uint32_t rows, uint32_t nb, uint32_t ldx, uint32_t tstep,
     const float* __restrict__ params, uint8_t* __restrict__ q, uint32_t ldq,
@@ -135,7 +160,8 @@ __global__ __launch_bounds__(kThreads) void butterfly_kernel(
   const uint32_t t = gtid / nb;
   if (t >= rows) return;
   // parameter loads first: the set-up then waits for them only
-  const BlockParams bp = load_params(params, b);
+  BlockParams bp;
+  if (MODE != kHadamard) bp = load_params(params, b);
   __builtin_amdgcn_sched_barrier(0);
   BlockConsts c;
   uint8_t* const qcol = q + b * (kBlk / 2);
@@ -143,37 +169,42 @@ __global__ __launch_bounds__(kThreads) void butterfly_kernel(
   uint8_t* const ycol = reinterpret_cast<uint8_t*>(y) + b * kBlk * 4;
   for_each_row<DT, kRowDepth>(
       x + (size_t)b * kBlk * (DT == DT_BF16 ? 2 : 4), rows, ldx, t, tstep,
-      [&] { make_consts<INV>(bp, c); },
+      [&] {
+        if (MODE != kHadamard) make_consts<MODE == kWeights>(bp, c);
+      },
       [&](float (&v)[kBlk], uint32_t r) {
-        transform<INV>(v, c);
+        if (MODE == kHadamard) hadamard(v);
+        else transform<MODE == kWeights>(v, c);
         if (WRITE_Y) store_y(reinterpret_cast<float*>(ycol + (uint64_t)r * ldy), v);
         encode_store(v, qcol + (uint64_t)r * ldq, scol + (uint64_t)r * lds);
       });
 }
 
-template <int DT, bool WRITE_Y, bool INV>
+template <int DT, bool WRITE_Y, int MODE>
 hipError_t launch_t(const LaunchArgs& a) {
   uint32_t tstep = 0;
   const int64_t grid = grid_for_units(a.rows, a.nb, a.cus, kBlocksPerCU, &tstep);
   const int64_t esz = DT == DT_BF16 ? 2 : 4;
-  hipLaunchKernelGGL((butterfly_kernel<DT, WRITE_Y, INV>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((butterfly_kernel<DT, WRITE_Y, MODE>), dim3((unsigned)grid), dim3(kThreads), 0,
                      (hipStream_t)a.stream, (const uint8_t*)a.x, (uint32_t)a.rows,
                      (uint32_t)a.nb, (uint32_t)(a.ldx * esz), tstep, (const float*)a.t, a.q,
                      (uint32_t)a.ldq, a.s, (uint32_t)a.lds, a.y, (uint32_t)(a.ldy * 4));
   return hipGetLastError();
 }
 
-template <bool INV>
-hipError_t launch_dir(const LaunchArgs& a) {
+template <int MODE>
+hipError_t launch_mode(const LaunchArgs& a) {
   if (a.dtype == DT_BF16)
-    return a.y ? launch_t<DT_BF16, true, INV>(a) : launch_t<DT_BF16, false, INV>(a);
-  return a.y ? launch_t<DT_FP32, true, INV>(a) : launch_t<DT_FP32, false, INV>(a);
+    return a.y ? launch_t<DT_BF16, true, MODE>(a) : launch_t<DT_BF16, false, MODE>(a);
+  return a.y ? launch_t<DT_FP32, true, MODE>(a) : launch_t<DT_FP32, false, MODE>(a);
 }
 
 }  // namespace
 
-hipError_t launch_butterfly(const LaunchArgs& a) { return launch_dir<false>(a); }
+hipError_t launch_butterfly(const LaunchArgs& a) { return launch_mode<kForward>(a); }
 
-hipError_t launch_weights(const LaunchArgs& a) { return launch_dir<true>(a); }
+hipError_t launch_weights(const LaunchArgs& a) { return launch_mode<kWeights>(a); }
+
+hipError_t launch_hadamard(const LaunchArgs& a) { return launch_mode<kHadamard>(a); }
 
 }  // namespace kq

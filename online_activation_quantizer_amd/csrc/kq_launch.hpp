@@ -59,7 +59,8 @@ inline int64_t grid_for_units(int64_t rows, int64_t nb, int cus, int blocks_per_
 }
 
 hipError_t launch_butterfly(const LaunchArgs& a);
-hipError_t launch_weights(const LaunchArgs& a);  // W T^-1 along each row, then MXFP4
+hipError_t launch_weights(const LaunchArgs& a);   // W T^-1 along each row, then MXFP4
+hipError_t launch_hadamard(const LaunchArgs& a);  // fixed block-Hadamard, then MXFP4
 hipError_t launch_sq(const LaunchArgs& a);
 hipError_t launch_mfma(const LaunchArgs& a);
 hipError_t launch_expand(const float* params, int64_t nb, int tfmt, void* out, void* stream);

@@ -23,7 +23,7 @@ KQ_AUTO, KQ_BUTTERFLY, KQ_MFMA = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
                     "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug",
-                    "kq_status_string", "kq_last_hip_error")
+                    "hq_quantize", "hq_transform_debug", "kq_status_string", "kq_last_hip_error")
 
 
 class KQError(RuntimeError):
@@ -53,6 +53,8 @@ def lib():
         L.sq_transform_debug.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I64, P]
         L.kq_quantize_weights.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P]
         L.kq_weights_debug.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I64, P]
+        L.hq_quantize.argtypes = [P, I, I64, I64, I64, P, I64, P, I64, P]
+        L.hq_transform_debug.argtypes = [P, I, I64, I64, I64, P, I64, P, I64, P, I64, P]
         L.kq_status_string.argtypes = [I]
         L.kq_status_string.restype = ctypes.c_char_p
         L.kq_last_hip_error.argtypes = []
@@ -187,4 +189,26 @@ def kq_weights_debug(w, params, q=None, s=None, y=None, stream=None):
     _check(lib().kq_weights_debug(w.data_ptr(), _dtype_code(w), rows, d, _row_pitch(w), params.data_ptr(),
                                   q.data_ptr(), _row_pitch(q), s.data_ptr(), _row_pitch(s),
                                   y.data_ptr(), _row_pitch(y), _stream(stream)), "kq_weights_debug")
+    return q, s, y
+
+
+def hq_quantize(x, q=None, s=None, stream=None):
+    """MXFP4 of the fixed block-Hadamard transform H x_b / sqrt(32) (comparison transform)."""
+    q, s = _outputs(x, q, s)
+    rows, d = x.shape
+    _check(lib().hq_quantize(x.data_ptr(), _dtype_code(x), rows, d, _row_pitch(x), q.data_ptr(),
+                             _row_pitch(q), s.data_ptr(), _row_pitch(s), _stream(stream)), "hq_quantize")
+    return q, s
+
+
+def hq_transform_debug(x, q=None, s=None, y=None, stream=None):
+    """hq_quantize that also returns the float32 transformed values y [rows, d]."""
+    import torch
+    q, s = _outputs(x, q, s)
+    rows, d = x.shape
+    if y is None:
+        y = torch.empty((rows, d), dtype=torch.float32, device=x.device)
+    _check(lib().hq_transform_debug(x.data_ptr(), _dtype_code(x), rows, d, _row_pitch(x), q.data_ptr(),
+                                    _row_pitch(q), s.data_ptr(), _row_pitch(s), y.data_ptr(), _row_pitch(y),
+                                    _stream(stream)), "hq_transform_debug")
     return q, s, y

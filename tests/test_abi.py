@@ -27,8 +27,8 @@ def header_functions(name="kq.h"):
 def test_header_symbols_exported(L):
     names = header_functions()
     assert {"kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
-            "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug", "kq_status_string",
-            "kq_last_hip_error"} <= set(names)
+            "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug", "hq_quantize",
+            "hq_transform_debug", "kq_status_string", "kq_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -117,6 +117,18 @@ def test_weights_validation(L):
     assert L.kq_quantize_weights(None, 0, 0, 64, 64, None, None, 32, None, 2, None) == OK
     assert L.kq_weights_debug(X, 0, 4, 64, 64, T, Q, 32, S, 2, None, 64, None) == NULL
     assert L.kq_weights_debug(X, 0, 4, 64, 64, T, Q, 32, S, 2, Y, 32, None) == SHAPE
+
+
+def test_hadamard_validation(L):
+    assert L.hq_quantize(None, 0, 4, 64, 64, Q, 32, S, 2, None) == NULL
+    assert L.hq_quantize(X, 0, 4, 64, 64, None, 32, S, 2, None) == NULL
+    assert L.hq_quantize(X, 0, 4, 64, 64, Q, 32, None, 2, None) == NULL
+    assert L.hq_quantize(X, 2, 4, 64, 64, Q, 32, S, 2, None) == DTYPE
+    assert L.hq_quantize(X, 0, 4, 40, 40, Q, 20, S, 2, None) == SHAPE
+    assert L.hq_quantize(X + 4, 0, 4, 64, 64, Q, 32, S, 2, None) == ALIGN
+    assert L.hq_quantize(None, 0, 0, 64, 64, None, 32, None, 2, None) == OK
+    assert L.hq_transform_debug(X, 0, 4, 64, 64, Q, 32, S, 2, None, 64, None) == NULL
+    assert L.hq_transform_debug(X, 0, 4, 64, 64, Q, 32, S, 2, Y, 63, None) == SHAPE
 
 
 def test_expand_validation(L):

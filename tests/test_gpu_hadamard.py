@@ -1,0 +1,66 @@
+"""The fixed block-Hadamard comparison transform (hq_quantize) against the fp64
+oracle, through the C ABI; same rule as the learned transform (pre-quantization
+values within 1e-5 * max|x_block|, codes and scales exact outside that window)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import online_activation_quantizer_amd as kq
+from gpu_util import dev, host, say, verdict
+
+pytestmark = pytest.mark.gpu
+
+
+def run_hq(x: np.ndarray):
+    import torch
+    xd = dev(x)
+    q, s = kq.hq_quantize(xd)
+    q2, s2, yd = kq.hq_transform_debug(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(s, s2), "debug and production kernels disagree"
+    return host(q), host(s), host(yd)
+
+
+@pytest.mark.parametrize("name", ["tiny", "pixart", "sana", "flux"])
+def test_hadamard_parity(name):
+    cfg = synth.get_config(name)
+    say(f"[hadamard parity] {name} {cfg.rows}x{cfg.d} {cfg.dtype}")
+    x, _, _ = synth.make_inputs(cfg)
+    q, s, y = run_hq(x)
+    _, _, y_o = oracle.hadamard_quantize(x, want_y=True)
+    st = verdict(x, y_o, q, s, y_c=y)
+    say(f"  {st}")
+    assert st["pass"], st
+
+
+@pytest.mark.parametrize("rows", [1, 7, 300])
+def test_hadamard_ragged_and_pitched(rows):
+    import torch
+    say(f"[hadamard ragged] rows={rows}")
+    rng = np.random.default_rng(rows)
+    full = synth.bf16_bits_from_f32(rng.normal(0, 3, size=(rows, 224)).astype(np.float32))
+    xd = dev(full)[:, :160]
+    q = torch.full((rows, 96), 0x5A, dtype=torch.uint8, device="cuda")
+    s = torch.full((rows, 16), 0xA5, dtype=torch.uint8, device="cuda")
+    kq.hq_quantize(xd, q=q[:, :80], s=s[:, :5])
+    torch.cuda.synchronize()
+    qh, sh = host(q), host(s)
+    assert np.all(qh[:, 80:] == 0x5A) and np.all(sh[:, 5:] == 0xA5)
+    x = np.ascontiguousarray(full[:, :160])
+    _, _, y_o = oracle.hadamard_quantize(x, want_y=True)
+    st = verdict(x, y_o, np.ascontiguousarray(qh[:, :80]), np.ascontiguousarray(sh[:, :5]))
+    assert st["pass"], st
+
+
+def test_hadamard_twice_is_identity_on_gpu():
+    import torch
+    say("[hadamard involution]")
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=(64, 256)).astype(np.float32)
+    _, _, y = kq.hq_transform_debug(dev(x))
+    _, _, z = kq.hq_transform_debug(y)
+    torch.cuda.synchronize()
+    err = np.abs(host(z) - x).max()
+    say(f"  max |H H x - x| = {err:.3g}")
+    assert err <= 1e-6 * np.abs(x).max()

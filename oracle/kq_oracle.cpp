@@ -312,6 +312,56 @@ int oq_hadamard_quantize(const void* x, int dtype, int64_t rows, int64_t d, int6
   return rc;
 }
 
+int oq_norm_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                     const float* shift, const float* scale, int64_t rows_per_sample, double eps,
+                     const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                     double* h_out, double* y_out, int nthreads) {
+  if (!x || !params || !q || !s || bad_shape(rows, d, ldx) ||
+      (dtype != OQ_BF16 && dtype != OQ_FP32) || ldq < d / 2 || lds < d / kBlk ||
+      rows_per_sample < 1 || !(eps >= 0.0))
+    return -1;
+  const int64_t nb = d / kBlk;
+  std::vector<double> T((size_t)nb * kBlk * kBlk);
+  oq_expand(params, nb, 0, T.data());
+  int rc = 0;
+  parallel_rows(rows, nthreads, [&](int64_t r0, int64_t r1) {
+    const int64_t n = r1 - r0;
+    std::vector<double> hbuf, ybuf;
+    double* h = h_out ? h_out + r0 * d : (hbuf.resize((size_t)n * d), hbuf.data());
+    double* y = y_out ? y_out + r0 * d : (ybuf.resize((size_t)n * d), ybuf.data());
+    for (int64_t t = 0; t < n; ++t) {
+      const int64_t row = r0 + t;
+      double* hr = h + t * d;
+      for (int64_t c = 0; c < d; ++c) hr[c] = oq_load(x, dtype, row * ldx + c);
+      // two-pass mean and (biased) variance
+      double mu = 0.0;
+      for (int64_t c = 0; c < d; ++c) mu += hr[c];
+      mu /= (double)d;
+      double var = 0.0;
+      for (int64_t c = 0; c < d; ++c) var += (hr[c] - mu) * (hr[c] - mu);
+      var /= (double)d;
+      const double rstd = 1.0 / std::sqrt(var + eps);
+      const int64_t g = row / rows_per_sample;
+      for (int64_t c = 0; c < d; ++c) {
+        const double sc = scale ? (double)scale[g * d + c] : 0.0;
+        const double sh = shift ? (double)shift[g * d + c] : 0.0;
+        hr[c] = (hr[c] - mu) * rstd * (1.0 + sc) + sh;
+      }
+      // y_b = T_b h_b
+      for (int64_t b = 0; b < nb; ++b) {
+        const double* Tb = T.data() + b * kBlk * kBlk;
+        for (int i = 0; i < kBlk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < kBlk; ++j) acc += Tb[i * kBlk + j] * hr[b * kBlk + j];
+          y[t * d + b * kBlk + i] = acc;
+        }
+      }
+    }
+    if (oq_encode(y, n, d, q + r0 * ldq, ldq, s + r0 * lds, lds) != 0) rc = -1;
+  });
+  return rc;
+}
+
 int oq_weight_transform(const void* w, int dtype, int64_t rows, int64_t d, int64_t ldw,
                         const float* params, double* w_out) {
   if (rows == 0 && !bad_shape(rows, d, ldw)) return 0;

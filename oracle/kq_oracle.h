@@ -119,6 +119,19 @@ int oq_hadamard_quantize(const void* x, int dtype, int64_t rows, int64_t d, int6
                          uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, double* y_out,
                          int nthreads);
 
+/* Normalization fused ahead of the quantizer ([ABS]: the normalization layers
+ * between blocks are what force the transform to run online).  Per row t
+ *   mu = mean_c x[t][c],  var = mean_c (x[t][c] - mu)^2,  rstd = 1 / sqrt(var + eps)
+ *   h[t][c] = (x[t][c] - mu) * rstd * (1 + scale[g][c]) + shift[g][c],  g = t / rows_per_sample
+ * (LayerNorm without affine parameters, then the adaptive-norm modulation of a DiT
+ * block; scale/shift may be NULL for zero), then y_b = T_b h_b and MXFP4.
+ * scale, shift: float32 [ceil(rows / rows_per_sample)][d].  h_out and y_out
+ * (optional, fp64 [rows][d]) receive h and y. */
+int oq_norm_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                     const float* shift, const float* scale, int64_t rows_per_sample, double eps,
+                     const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                     double* h_out, double* y_out, int nthreads);
+
 /* Parity accounting of candidate outputs against the oracle's fp64 values y_o.
  * Per block the tolerance is tol_coef * max|x_blk| (tol_mode 0, the fp32 rule) or
  * tol_coef * max|y_o_blk| (tol_mode 1, the block-relative bf16 rule).

@@ -59,6 +59,8 @@ def lib():
         L.oq_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
         L.oq_sq_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
         L.oq_hadamard_quantize.argtypes = [P, I, I64, I64, I64, P, I64, P, I64, P, I]
+        L.oq_norm_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, ctypes.c_double, P, P, I64, P, I64,
+                                       P, P, I]
         L.oq_weight_transform.argtypes = [P, I, I64, I64, I64, P, P]
         L.oq_quantize_weights.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
         L.oq_classify.argtypes = [P, I, I64, I64, I64, P, I, D, P, I64, P, I64, P, I64, P]
@@ -201,6 +203,27 @@ def hadamard_quantize(x: np.ndarray, want_y: bool = False, nthreads: int = 0):
                                     _ptr(y) if want_y else None, nthreads)
     _check(rc, "hadamard_quantize")
     return q, s, y
+
+
+def norm_quantize(x: np.ndarray, params: np.ndarray, shift=None, scale=None, rows_per_sample=None,
+                  eps: float = 1e-6, want_y: bool = False, nthreads: int = 0):
+    """(q, s, h fp64, y fp64 or None): LayerNorm (no affine) + adaptive-norm modulation
+    (1 + scale) * . + shift per sample, then the block transform and MXFP4."""
+    dt, rows, ldx = _x_info(x)
+    d = x.shape[1]
+    p = np.ascontiguousarray(params, np.float32)
+    rps = rows if rows_per_sample is None else rows_per_sample
+    sh = None if shift is None else np.ascontiguousarray(shift, np.float32)
+    sc = None if scale is None else np.ascontiguousarray(scale, np.float32)
+    q = np.zeros((rows, d // 2), np.uint8)
+    s = np.zeros((rows, d // 32), np.uint8)
+    h = np.zeros((rows, d), np.float64)
+    y = np.zeros((rows, d), np.float64) if want_y else None
+    rc = lib().oq_norm_quantize(_ptr(x), dt, rows, d, ldx, _ptr(sh) if sh is not None else None,
+                                _ptr(sc) if sc is not None else None, max(1, rps), eps, _ptr(p), _ptr(q),
+                                d // 2, _ptr(s), d // 32, _ptr(h), _ptr(y) if want_y else None, nthreads)
+    _check(rc, "norm_quantize")
+    return q, s, h, y
 
 
 def weight_transform(w: np.ndarray, params: np.ndarray) -> np.ndarray:

@@ -61,6 +61,15 @@ MUTANTS = {
     "hadamard_scale_dropped": (
         "y[t * d + b * kBlk + i] = acc * norm;",
         "y[t * d + b * kBlk + i] = acc;"),
+    "norm_unbiased_variance": (
+        "      var /= (double)d;",
+        "      var /= (double)(d - 1);"),
+    "norm_scale_without_one": (
+        "hr[c] = (hr[c] - mu) * rstd * (1.0 + sc) + sh;",
+        "hr[c] = (hr[c] - mu) * rstd * sc + sh;"),
+    "norm_sample_index_modulo": (
+        "const int64_t g = row / rows_per_sample;",
+        "const int64_t g = row % rows_per_sample;"),
     "amax_without_abs": (
         "        amax = std::max(amax, std::fabs(yb[i]));\n      }\n      uint8_t* qb",
         "        amax = std::max(amax, yb[i]);\n      }\n      uint8_t* qb"),

@@ -375,3 +375,47 @@ def test_hadamard_exact_cancellation_is_positive_zero(oq):
     q, s, y = oq.hadamard_quantize(x, want_y=True)
     assert np.all(y[0, 1::2] == 0.0) and not np.any(np.signbit(y[0, 1::2]))
     assert np.all((q[0] >> 4) == 0)  # odd channels sit in the high nibbles
+
+
+# ------------------------------------------------------------------ fused normalization
+
+def test_norm_closed_form_row(oq):
+    # x = 0, 1, ..., 31: mean 15.5, biased variance (32^2 - 1) / 12 = 85.25
+    x = np.arange(32, dtype=np.float32).reshape(1, 32)
+    q, s, h, y = oq.norm_quantize(x, synth.make_identity_params(1), eps=0.0, want_y=True)
+    expect = (np.arange(32) - 15.5) / np.sqrt(85.25)
+    np.testing.assert_allclose(h[0], expect, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(y[0], expect, rtol=0, atol=1e-14)  # identity factors
+    q2, s2 = oq.encode(y)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+def test_norm_moments_and_eps(oq):
+    rng = np.random.default_rng(51)
+    x = (rng.normal(size=(6, 96)) * 3 + 5).astype(np.float32)
+    p = synth.make_identity_params(3)
+    _, _, h, _ = oq.norm_quantize(x, p, eps=0.0)
+    np.testing.assert_allclose(h.mean(1), 0.0, atol=1e-13)
+    np.testing.assert_allclose((h ** 2).mean(1), 1.0, rtol=1e-13)
+    eps = 0.5
+    _, _, he, _ = oq.norm_quantize(x, p, eps=eps)
+    var = x.astype(np.float64).var(1)
+    np.testing.assert_allclose((he ** 2).mean(1), var / (var + eps), rtol=1e-12)
+
+
+def test_norm_shift_invariance_and_modulation_per_sample(oq):
+    rng = np.random.default_rng(52)
+    x = (rng.integers(-64, 64, size=(7, 64)) / 8.0).astype(np.float32)  # exact after + 3
+    p = synth.make_params(2, rng)
+    _, _, h0, y0 = oq.norm_quantize(x, p, want_y=True)
+    _, _, h1, _ = oq.norm_quantize((x + 3).astype(np.float32), p)
+    np.testing.assert_allclose(h1, h0, rtol=0, atol=1e-12)
+    scale = rng.normal(0, 0.3, size=(3, 64)).astype(np.float32)
+    shift = rng.normal(0, 0.5, size=(3, 64)).astype(np.float32)
+    _, _, hm, ym = oq.norm_quantize(x, p, shift=shift, scale=scale, rows_per_sample=3, want_y=True)
+    g = np.arange(7) // 3  # rows 0-2 sample 0, 3-5 sample 1, 6 sample 2
+    np.testing.assert_allclose(hm, h0 * (1 + scale[g].astype(np.float64)) + shift[g], rtol=0, atol=1e-12)
+    # the transform of the modulated rows, by numpy from the dense T_b
+    T = oq.expand(p)
+    ref = np.einsum("bij,rbj->rbi", T, hm.reshape(7, 2, 32)).reshape(7, 64)
+    np.testing.assert_allclose(ym, ref, rtol=0, atol=1e-12 * np.abs(ref).max())

@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-sq", action="store_true",
                     help="skip the SmoothQuant and block-Hadamard comparison timings")
     ap.add_argument("--no-weights", action="store_true", help="skip the weight-side timing")
+    ap.add_argument("--no-norm", action="store_true",
+                    help="skip the normalization-fused quantizer timing")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the same-bytes streaming kernel (practical HBM ceiling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -162,6 +164,45 @@ def stream_ceiling(args, xs, qs, ss, kq_ms):
             "grid": grid, "kq_time_over_ceiling_time": round(kq_ms / ms, 4)}
 
 
+def norm_timing(args, cfg, xs, ps, qs, ss, kq_ms):
+    """LayerNorm + adaptive-norm modulation fused ahead of the quantizer
+    (kq_norm_quantize) on the same pool, against the unfused sequence it replaces
+    as torch runs it: layer_norm, then the modulation (addcmul), both in bf16 with
+    their outputs written to and re-read from HBM, then kq_quantize."""
+    import torch
+
+    import synth
+    import online_activation_quantizer_amd as kq
+    P = len(xs)
+    shift, scale = synth.make_modulation(1, cfg.d, np.random.default_rng(cfg.seed + 77))
+    shd, scd = torch.from_numpy(shift).cuda(), torch.from_numpy(scale).cuda()
+    xb = [x.view(torch.bfloat16) for x in xs]
+    hbuf = torch.empty((cfg.rows, cfg.d), dtype=torch.bfloat16, device="cuda")
+    sc_b, sh_b = (1 + scd).to(torch.bfloat16), shd.to(torch.bfloat16)
+
+    def fused(i):
+        j = i % P
+        kq.kq_norm_quantize(xs[j], ps[j], shd, scd, cfg.rows, 1e-6, q=qs[j], s=ss[j])
+
+    def unfused(i):
+        j = i % P
+        h = torch.nn.functional.layer_norm(xb[j], (cfg.d,), eps=1e-6)
+        torch.addcmul(sh_b, h, sc_b, out=hbuf)
+        kq.kq_quantize(hbuf.view(torch.int16), ps[j], q=qs[j], s=ss[j])
+
+    run = (lambda f, n: timed(f, n, args.warmup, torch.cuda.current_stream())) if args.eager else \
+        (lambda f, n: timed_graph(f, n, args.warmup))
+    steps = max(8, args.steps // 4)
+    f_ms = run(fused, steps)
+    u_ms = run(unfused, steps)
+    elems = cfg.rows * cfg.d
+    gbs = elems * BYTES_PER_ELEM / (f_ms * 1e-3) / 1e9
+    return {"workload": f"{cfg.rows}x{cfg.d} bf16 pre-norm activations, 1 modulation vector",
+            "ms_per_call": round(f_ms, 6), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "unfused_ms_per_call": round(u_ms, 6), "unfused_over_fused": round(u_ms / f_ms, 4),
+            "fused_over_quantizer_alone": round(f_ms / kq_ms, 4)}
+
+
 def weights_timing(args):
     """The weight side (W T^-1 then MXFP4 along the input channels) on the FLUX MLP
     up-projection W[12288, 3072] bf16, timed like the activation step over 4
@@ -257,6 +298,7 @@ def main():
         hq_ms = None if args.no_sq else timed_graph(hq_step, args.steps, args.warmup)
 
     weights = None if args.no_weights else weights_timing(args)
+    norm = None if args.no_norm else norm_timing(args, cfg, xs, ps, qs, ss, ms)
     ceiling = None if args.no_ceiling else stream_ceiling(args, xs, qs, ss, ms)
 
     # parity of one production step against the oracle
@@ -309,6 +351,8 @@ def main():
         out["stream_ceiling"] = ceiling
     if weights is not None:
         out["weights"] = weights
+    if norm is not None:
+        out["norm_fused"] = norm
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -67,7 +67,8 @@ typedef enum {
   KQ_ERR_FORMAT = -5,   /* unknown transform format, or one the variant
                            cannot consume                                    */
   KQ_ERR_VARIANT = -6,  /* unknown variant                                  */
-  KQ_ERR_HIP = -7       /* a HIP call failed                                */
+  KQ_ERR_HIP = -7,      /* a HIP call failed                                */
+  KQ_ERR_VALUE = -8     /* a scalar argument out of range (eps)             */
 } kq_status;
 
 typedef enum { KQ_BF16 = 0, KQ_FP32 = 1 } kq_dtype;
@@ -173,6 +174,34 @@ int hq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, 
 int hq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
                        uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, float* y, int64_t ldy,
                        void* stream);
+
+/* Normalization fused ahead of the quantizer (KroQuant abstract: the
+ * normalization layers between blocks are what force the transform to run online
+ * at every step).  For every row t of the pre-normalization activations x:
+ *   mu, var = mean and biased variance of x[t][0 .. d-1];  rstd = 1/sqrt(var + eps)
+ *   h[t][c] = (x[t][c] - mu) * rstd * (1 + scale[g][c]) + shift[g][c],  g = t / rows_per_sample
+ * (LayerNorm without affine parameters followed by the adaptive-norm modulation of
+ * a DiT block), then y_b = T_b h_b and the MXFP4 encoding, as kq_quantize.  The
+ * row is read from HBM once; nothing intermediate is written.
+ *   shift, scale     device float32 [ceil(rows / rows_per_sample)][d], 16-byte
+ *                    aligned; both NULL for a plain LayerNorm (one NULL alone is
+ *                    KQ_ERR_NULL)
+ *   rows_per_sample  rows (tokens) per modulation vector, >= 1
+ *   eps              >= 0, finite (KQ_ERR_VALUE otherwise)
+ *   params           device float32 [d/32][5][3] (KQ_T_PARAMS format)
+ * Computed in fp32: shifted sums for the statistics, one wave per row.
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_DTYPE, KQ_ERR_VALUE, KQ_ERR_HIP. */
+int kq_norm_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                     const float* shift, const float* scale, int64_t rows_per_sample, float eps,
+                     const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                     void* stream);
+
+/* Validation entry of kq_norm_quantize: also writes the float32 y (after the
+ * transform, before quantization) into y [rows][ldy] (ldy >= d, 4-byte aligned). */
+int kq_norm_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                  const float* shift, const float* scale, int64_t rows_per_sample, float eps,
+                  const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, float* y,
+                  int64_t ldy, void* stream);
 
 /* Static text for a kq_status value (never NULL). */
 const char* kq_status_string(int status);

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <climits>
+#include <cmath>
 
 #include "kq_launch.hpp"
 
@@ -174,6 +175,32 @@ int hadamard_impl(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx
   return e == hipSuccess ? KQ_OK : fail_hip(e);
 }
 
+int norm_impl(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, const float* shift,
+              const float* scale, int64_t rows_per_sample, float eps, const float* params,
+              uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, float* y, int64_t ldy, bool debug,
+              void* stream) {
+  int rc = check_common(x, dtype, rows, d, ldx, params, q, ldq, s, lds);
+  if (rc != KQ_OK) return rc;
+  if (rows_per_sample < 1) return KQ_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return KQ_ERR_VALUE;
+  if (debug) {
+    if (ldy < d || ldy * 4 > kMaxPitch) return KQ_ERR_SHAPE;
+    if (rows > 0 && !y) return KQ_ERR_NULL;
+    if (rows > 0 && !aligned(y, 4)) return KQ_ERR_ALIGN;
+  }
+  if (rows == 0) return KQ_OK;
+  if ((shift == nullptr) != (scale == nullptr)) return KQ_ERR_NULL;
+  if (!aligned(params, 4) || (shift && (!aligned(shift, 16) || !aligned(scale, 16))))
+    return KQ_ERR_ALIGN;
+  kq::NormArgs n{{x, dtype, rows, d, d / 32, ldx, params, q, ldq, s, lds, debug ? y : nullptr,
+                  ldy, stream, 0},
+                 shift, scale, rows_per_sample < rows ? rows_per_sample : rows, eps};
+  rc = current_cus(&n.a.cus);
+  if (rc != KQ_OK) return rc;
+  const hipError_t e = kq::launch_norm(n);
+  return e == hipSuccess ? KQ_OK : fail_hip(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -237,6 +264,22 @@ int hq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_
   return hadamard_impl(x, dtype, rows, d, ldx, q, ldq, s, lds, y, ldy, true, stream);
 }
 
+int kq_norm_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                     const float* shift, const float* scale, int64_t rows_per_sample, float eps,
+                     const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                     void* stream) {
+  return norm_impl(x, dtype, rows, d, ldx, shift, scale, rows_per_sample, eps, params, q, ldq, s,
+                   lds, nullptr, 0, false, stream);
+}
+
+int kq_norm_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
+                  const float* shift, const float* scale, int64_t rows_per_sample, float eps,
+                  const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, float* y,
+                  int64_t ldy, void* stream) {
+  return norm_impl(x, dtype, rows, d, ldx, shift, scale, rows_per_sample, eps, params, q, ldq, s,
+                   lds, y, ldy, true, stream);
+}
+
 const char* kq_status_string(int status) {
   switch (status) {
     case KQ_OK: return "ok";
@@ -247,6 +290,7 @@ const char* kq_status_string(int status) {
     case KQ_ERR_FORMAT: return "unsupported transform format";
     case KQ_ERR_VARIANT: return "unknown variant";
     case KQ_ERR_HIP: return "HIP error";
+    case KQ_ERR_VALUE: return "scalar argument out of range";
     default: return "unknown status";
   }
 }

@@ -33,6 +33,17 @@ struct LaunchArgs {
   int cus;  // compute units of the current device
 };
 
+// Normalization-fused quantizer: the quantize arguments plus the modulation.
+struct NormArgs {
+  LaunchArgs a;
+  const float* shift;  // [samples][d] or NULL (then scale is NULL too)
+  const float* scale;
+  int64_t rows_per_sample;
+  float eps;
+};
+// Resident-grid target of the row-per-wave normalization kernel.
+constexpr int kNormBlocksPerCU = 4;
+
 inline int64_t gcd64(int64_t a, int64_t b) {
   while (b) {
     const int64_t r = a % b;
@@ -61,6 +72,7 @@ inline int64_t grid_for_units(int64_t rows, int64_t nb, int cus, int blocks_per_
 hipError_t launch_butterfly(const LaunchArgs& a);
 hipError_t launch_weights(const LaunchArgs& a);   // W T^-1 along each row, then MXFP4
 hipError_t launch_hadamard(const LaunchArgs& a);  // fixed block-Hadamard, then MXFP4
+hipError_t launch_norm(const NormArgs& n);        // LayerNorm + modulation, T_b, MXFP4
 hipError_t launch_sq(const LaunchArgs& a);
 hipError_t launch_mfma(const LaunchArgs& a);
 hipError_t launch_expand(const float* params, int64_t nb, int tfmt, void* out, void* stream);

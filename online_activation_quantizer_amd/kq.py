@@ -14,16 +14,18 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkq.so")
 
 KQ_OK, KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN = 0, -1, -2, -3
-KQ_ERR_DTYPE, KQ_ERR_FORMAT, KQ_ERR_VARIANT, KQ_ERR_HIP = -4, -5, -6, -7
+KQ_ERR_DTYPE, KQ_ERR_FORMAT, KQ_ERR_VARIANT, KQ_ERR_HIP, KQ_ERR_VALUE = -4, -5, -6, -7, -8
 STATUS = {0: "KQ_OK", -1: "KQ_ERR_NULL", -2: "KQ_ERR_SHAPE", -3: "KQ_ERR_ALIGN",
-          -4: "KQ_ERR_DTYPE", -5: "KQ_ERR_FORMAT", -6: "KQ_ERR_VARIANT", -7: "KQ_ERR_HIP"}
+          -4: "KQ_ERR_DTYPE", -5: "KQ_ERR_FORMAT", -6: "KQ_ERR_VARIANT", -7: "KQ_ERR_HIP",
+          -8: "KQ_ERR_VALUE"}
 KQ_BF16, KQ_FP32 = 0, 1
 KQ_T_PARAMS, KQ_T_DENSE_F32, KQ_T_DENSE_BF16X3 = 0, 1, 2
 KQ_AUTO, KQ_BUTTERFLY, KQ_MFMA = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
                     "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug",
-                    "hq_quantize", "hq_transform_debug", "kq_status_string", "kq_last_hip_error")
+                    "hq_quantize", "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug",
+                    "kq_status_string", "kq_last_hip_error")
 
 
 class KQError(RuntimeError):
@@ -55,6 +57,9 @@ def lib():
         L.kq_weights_debug.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I64, P]
         L.hq_quantize.argtypes = [P, I, I64, I64, I64, P, I64, P, I64, P]
         L.hq_transform_debug.argtypes = [P, I, I64, I64, I64, P, I64, P, I64, P, I64, P]
+        F = ctypes.c_float
+        L.kq_norm_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, F, P, P, I64, P, I64, P]
+        L.kq_norm_debug.argtypes = [P, I, I64, I64, I64, P, P, I64, F, P, P, I64, P, I64, P, I64, P]
         L.kq_status_string.argtypes = [I]
         L.kq_status_string.restype = ctypes.c_char_p
         L.kq_last_hip_error.argtypes = []
@@ -211,4 +216,37 @@ def hq_transform_debug(x, q=None, s=None, y=None, stream=None):
     _check(lib().hq_transform_debug(x.data_ptr(), _dtype_code(x), rows, d, _row_pitch(x), q.data_ptr(),
                                     _row_pitch(q), s.data_ptr(), _row_pitch(s), y.data_ptr(), _row_pitch(y),
                                     _stream(stream)), "hq_transform_debug")
+    return q, s, y
+
+
+def _ptr_or_null(t):
+    return None if t is None else t.data_ptr()
+
+
+def kq_norm_quantize(x, params, shift=None, scale=None, rows_per_sample=None, eps: float = 1e-6,
+                     q=None, s=None, stream=None):
+    """LayerNorm + (1 + scale) * . + shift per sample, block transform, MXFP4 (x before normalization)."""
+    q, s = _outputs(x, q, s)
+    rows, d = x.shape
+    rps = rows if rows_per_sample is None else rows_per_sample
+    _check(lib().kq_norm_quantize(x.data_ptr(), _dtype_code(x), rows, d, _row_pitch(x), _ptr_or_null(shift),
+                                  _ptr_or_null(scale), max(1, rps), eps, params.data_ptr(), q.data_ptr(),
+                                  _row_pitch(q), s.data_ptr(), _row_pitch(s), _stream(stream)),
+           "kq_norm_quantize")
+    return q, s
+
+
+def kq_norm_debug(x, params, shift=None, scale=None, rows_per_sample=None, eps: float = 1e-6, q=None,
+                  s=None, y=None, stream=None):
+    """kq_norm_quantize that also returns the float32 transformed values y [rows, d]."""
+    import torch
+    q, s = _outputs(x, q, s)
+    rows, d = x.shape
+    rps = rows if rows_per_sample is None else rows_per_sample
+    if y is None:
+        y = torch.empty((rows, d), dtype=torch.float32, device=x.device)
+    _check(lib().kq_norm_debug(x.data_ptr(), _dtype_code(x), rows, d, _row_pitch(x), _ptr_or_null(shift),
+                               _ptr_or_null(scale), max(1, rps), eps, params.data_ptr(), q.data_ptr(),
+                               _row_pitch(q), s.data_ptr(), _row_pitch(s), y.data_ptr(), _row_pitch(y),
+                               _stream(stream)), "kq_norm_debug")
     return q, s, y

@@ -107,3 +107,11 @@ def make_weights(cfg: WeightConfig, seed: int | None = None):
     if cfg.dtype == "bf16":
         return bf16_bits_from_f32(w), params
     return np.ascontiguousarray(w, np.float32), params
+
+
+def make_modulation(n_samples: int, d: int, rng: np.random.Generator):
+    """(shift, scale) float32 [n_samples, d] of the adaptive-norm modulation:
+    scale ~ N(0, 0.3), shift ~ N(0, 0.5), drawn in that order."""
+    scale = rng.normal(0.0, 0.3, size=(n_samples, d)).astype(np.float32)
+    shift = rng.normal(0.0, 0.5, size=(n_samples, d)).astype(np.float32)
+    return shift, scale

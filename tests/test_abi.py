@@ -28,7 +28,8 @@ def test_header_symbols_exported(L):
     names = header_functions()
     assert {"kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
             "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug", "hq_quantize",
-            "hq_transform_debug", "kq_status_string", "kq_last_hip_error"} <= set(names)
+            "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug", "kq_status_string",
+            "kq_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -131,6 +132,26 @@ def test_hadamard_validation(L):
     assert L.hq_transform_debug(X, 0, 4, 64, 64, Q, 32, S, 2, Y, 63, None) == SHAPE
 
 
+def test_norm_validation(L):
+    def norm(x=X, dtype=0, rows=4, d=64, ldx=64, shift=Y, scale=Y + 256, rps=4, eps=1e-6, p=T, q=Q,
+             ldq=32, s=S, lds=2):
+        return L.kq_norm_quantize(x, dtype, rows, d, ldx, shift, scale, rps, eps, p, q, ldq, s, lds, None)
+    assert norm(rps=0) == SHAPE
+    assert norm(eps=-1.0) == -8
+    assert norm(eps=float("nan")) == -8
+    assert norm(eps=float("inf")) == -8
+    assert norm(shift=None) == NULL          # one modulation vector alone
+    assert norm(scale=None) == NULL
+    assert norm(shift=Y + 4) == ALIGN
+    assert norm(p=None) == NULL
+    assert norm(p=T + 2) == ALIGN
+    assert norm(dtype=9) == DTYPE
+    assert norm(d=48, ldx=48) == SHAPE
+    assert norm(x=None, rows=0, p=None, q=None, s=None) == OK
+    assert L.kq_norm_debug(X, 0, 4, 64, 64, None, None, 4, 1e-6, T, Q, 32, S, 2, None, 64, None) == NULL
+    assert L.kq_status_string(-8) == b"scalar argument out of range"
+
+
 def test_expand_validation(L):
     assert L.kq_expand_factors(T, 4, 0, Y, None) == FORMAT  # params need no expansion
     assert L.kq_expand_factors(T, 4, 7, Y, None) == FORMAT
@@ -142,7 +163,7 @@ def test_expand_validation(L):
 
 
 def test_status_strings(L):
-    for st in range(-7, 1):
+    for st in range(-8, 1):
         assert L.kq_status_string(st)
     assert L.kq_status_string(-100) == b"unknown status"
     assert L.kq_last_hip_error() == 0

@@ -99,7 +99,7 @@ def timed_graph(fn, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
-KERNEL_SOURCES = ("kq_butterfly.hip", "kq_device.hpp", "kq_launch.hpp")
+KERNEL_SOURCES = ("kq_butterfly.hip", "kq_device.hpp", "kq_factors.hpp", "kq_launch.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kq_butterfly_flux_4608x3072_traffic.json")
 
 

@@ -189,7 +189,9 @@ int hq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_
  *   rows_per_sample  rows (tokens) per modulation vector, >= 1
  *   eps              >= 0, finite (KQ_ERR_VALUE otherwise)
  *   params           device float32 [d/32][5][3] (KQ_T_PARAMS format)
- * Computed in fp32: shifted sums for the statistics, one wave per row.
+ * d is at most 16384 here (one row per workgroup; KQ_ERR_SHAPE beyond).
+ * Computed in fp32: per-block moments merged pairwise for the statistics, the
+ * modulation folded into the transform's diagonal plus a constant T_b shift.
  * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_DTYPE, KQ_ERR_VALUE, KQ_ERR_HIP. */
 int kq_norm_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
                      const float* shift, const float* scale, int64_t rows_per_sample, float eps,

@@ -48,6 +48,8 @@ int current_cus(int* cus) {
 constexpr int64_t kMaxBlocks = int64_t(1) << 22;
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxPitch = (int64_t(1) << 32) - 1;
+// The normalization-fused kernel holds one row per workgroup: at most 512 blocks.
+constexpr int64_t kMaxNormWidth = 16384;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -181,7 +183,7 @@ int norm_impl(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, co
               void* stream) {
   int rc = check_common(x, dtype, rows, d, ldx, params, q, ldq, s, lds);
   if (rc != KQ_OK) return rc;
-  if (rows_per_sample < 1) return KQ_ERR_SHAPE;
+  if (rows_per_sample < 1 || d > kMaxNormWidth) return KQ_ERR_SHAPE;
   if (!(eps >= 0.0f) || !std::isfinite(eps)) return KQ_ERR_VALUE;
   if (debug) {
     if (ldy < d || ldy * 4 > kMaxPitch) return KQ_ERR_SHAPE;

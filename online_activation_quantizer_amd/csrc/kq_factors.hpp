@@ -106,10 +106,9 @@ __device__ __forceinline__ void hadamard(float (&v)[kBlk]) {
 
 // T_b x (upper shears by u v, then lower by l) or, for INV, T_b^-T x (lower shears
 // by -u v, then upper by -l), after the diagonal.
+// The shear part alone (what follows the diagonal).
 template <bool INV>
-__device__ __forceinline__ void transform(float (&v)[kBlk], const BlockConsts& c) {
-#pragma unroll
-  for (int i = 0; i < kBlk; ++i) v[i] *= c.d[i];
+__device__ __forceinline__ void shears(float (&v)[kBlk], const BlockConsts& c) {
   if (INV) {
     lower_shears(v, c.su);
     upper_shears(v, c.ll);
@@ -117,6 +116,13 @@ __device__ __forceinline__ void transform(float (&v)[kBlk], const BlockConsts& c
     upper_shears(v, c.su);
     lower_shears(v, c.ll);
   }
+}
+
+template <bool INV>
+__device__ __forceinline__ void transform(float (&v)[kBlk], const BlockConsts& c) {
+#pragma unroll
+  for (int i = 0; i < kBlk; ++i) v[i] *= c.d[i];
+  shears<INV>(v, c);
 }
 
 }  // namespace

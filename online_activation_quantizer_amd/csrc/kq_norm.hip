@@ -8,16 +8,28 @@
 //   h = (x - mu) * rstd * (1 + scale[g]) + shift[g],   g = t / rows_per_sample,
 // then y_b = T_b h_b per 32-channel block and the MXFP4 encoding of y.
 //
-// One wave owns one row at a time (rows in a grid-stride loop).  Pass 1 reads the
-// row (lane l takes blocks l, l + 64, ...) and computes each block's mean (pairwise
-// sum) and sum of squared deviations from it; blocks, then lanes (a butterfly of
-// lane exchanges), are merged with the pairwise update of Chan, Golub and LeVeque
-// (count, mean, M2), which keeps the statistics accurate to a few ulps whatever
-// the row's mean and outliers.  Pass 2 reads the row again (it was just read: the re-read is served by
-// the cache, not by HBM), normalizes, modulates, applies the factored transform
-// from the block's factors and encodes.  HBM traffic stays the quantizer's
-// 2.53125 B per element (plus the modulation vectors, shared by all rows of a
-// sample).
+// Mapping.  A row is handled by H = ceil(nb / 32) half waves, one lane per block
+// (lanes past nb idle), and a workgroup holds R = max(1, 256 / 32H) rows packed
+// back to back, so every lane keeps one block for the whole kernel and walks rows
+// with a stride of R x gridDim.x, loading the next row while it works on the
+// current one.
+//
+// Statistics.  Each lane takes its block's mean (pairwise sum) and sum of squared
+// deviations; the 32 lanes of a half wave are merged with the pairwise update of
+// Chan, Golub and LeVeque (count, mean, M2) by a butterfly of lane exchanges, and
+// the H half-wave partials of a row through LDS (one barrier per row), always in
+// the same order, so the result is deterministic and accurate whatever the row's
+// mean and outliers.
+//
+// Arithmetic.  With T_b = (kron L)(kron S) diag(d) and h = n * a + sh, where
+// n = (x - mu) * rstd and a = 1 + scale:
+//     y = rstd * (kron L)(kron S) diag(d * a) (x - mu) + T_b sh,
+// so the modulation folds into the transform's diagonal (e = d * a) and a constant
+// c = T_b sh, both computed once per lane and sample.  Per element that is one
+// subtraction more and one fma (y = rstd * z + c) than the quantizer alone.
+//
+// Traffic: the quantizer's 2.53125 B per element plus the modulation vectors,
+// read once per lane and sample.
 #include "kq_device.hpp"
 #include "kq_factors.hpp"
 #include "kq_launch.hpp"
@@ -35,7 +47,7 @@ __device__ __forceinline__ Moments merge(const Moments& a, const Moments& b) {
   const float n = a.n + b.n;
   if (n == 0.0f) return a;
   const float delta = b.mean - a.mean;
-  const float wb = b.n / n;
+  const float wb = b.n * __builtin_amdgcn_rcpf(n);  // exact for the power-of-two counts
   return {n, __builtin_fmaf(delta, wb, a.mean), a.m2 + b.m2 + delta * delta * (a.n * wb)};
 }
 
@@ -59,9 +71,10 @@ __device__ __forceinline__ Moments block_moments(const float (&v)[kBlk]) {
   return {(float)kBlk, mean, m2};
 }
 
-__device__ __forceinline__ Moments wave_merge(Moments m) {
+// Merge over the 32 lanes of a half wave (every lane ends with the same result).
+__device__ __forceinline__ Moments half_merge(Moments m) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
+  for (int off = 16; off >= 1; off >>= 1) {
     const Moments o = {__shfl_xor(m.n, off), __shfl_xor(m.mean, off), __shfl_xor(m.m2, off)};
     // both lanes of a pair merge in the same order so they end with equal values
     m = (threadIdx.x & off) ? merge(o, m) : merge(m, o);
@@ -69,74 +82,146 @@ __device__ __forceinline__ Moments wave_merge(Moments m) {
   return m;
 }
 
+constexpr uint32_t kMaxNormHalves = 16;  // half waves per workgroup (512 threads: d <= 16384)
+
 template <int DT, bool MOD, bool WRITE_Y>
-__global__ __launch_bounds__(kThreads) void norm_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(3))) void norm_kernel(
     const uint8_t* __restrict__ x, uint32_t rows, uint32_t nb, uint32_t ldx,
     const float* __restrict__ shift, const float* __restrict__ scale, uint32_t rows_per_sample,
     float eps, float inv_d, const float* __restrict__ params, uint8_t* __restrict__ q,
-    uint32_t ldq, uint8_t* __restrict__ s, uint32_t lds, float* __restrict__ y, uint32_t ldy) {
-  // pitches in bytes; one wave per row
+    uint32_t ldq, uint8_t* __restrict__ s, uint32_t lds, float* __restrict__ y, uint32_t ldy,
+    uint32_t H, uint32_t R) {
+  // pitches in bytes; a row takes H half waves (32 H >= nb lanes), R rows per
+  // workgroup, blockDim.x = 32 H R rounded up to whole waves
+  __shared__ float part[2][kMaxNormHalves][3];
   constexpr uint32_t kBlkBytes = kBlk * (DT == DT_BF16 ? 2 : 4);
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t nwaves = gridDim.x * (kThreads / 64);
+  const uint32_t L = 32u * H;
+  const uint32_t half = threadIdx.x >> 5;
+  const uint32_t slot0 = threadIdx.x / L, b = threadIdx.x - slot0 * L;
+  const bool active = slot0 < R && b < nb;
+  const uint32_t slot = slot0 < R ? slot0 : R - 1;
+  const uint32_t bb = b < nb ? b : nb - 1;  // idle lanes shadow a real block, store nothing
+  const uint32_t last = rows - 1;
+  const uint32_t rstep = gridDim.x * R;
   const uint64_t d = (uint64_t)nb * kBlk;
-  for (uint32_t r = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < rows; r += nwaves) {
-    const uint8_t* xr = x + (uint64_t)r * ldx;
-    Moments m = {0.0f, 0.0f, 0.0f};
-    for (uint32_t b = lane; b < nb; b += 64) {
-      float v[kBlk];
-      unpack(load_raw<DT>(xr + (uint64_t)b * kBlkBytes), v);
-      m = merge(m, block_moments(v));
-    }
-    m = wave_merge(m);
-    const float mean = m.mean;
-    const float var = m.m2 * inv_d;
-    const float rstd = 1.0f / __builtin_sqrtf(var + eps);
-    const uint64_t g = r / rows_per_sample;
-    for (uint32_t b = lane; b < nb; b += 64) {
-      const BlockParams bp = load_params(params, b);
-      float v[kBlk];
-      unpack(load_raw<DT>(xr + (uint64_t)b * kBlkBytes), v);
-      BlockConsts c;
-      make_consts<false>(bp, c);
-      if (MOD) {
-        const float4* sc4 = reinterpret_cast<const float4*>(scale + g * d + (uint64_t)b * kBlk);
-        const float4* sh4 = reinterpret_cast<const float4*>(shift + g * d + (uint64_t)b * kBlk);
+  const uint8_t* const xcol = x + (uint64_t)bb * kBlkBytes;
+
+  // rows of this lane: r0 + k * rstep; the workgroup iterates while its first slot's
+  // row exists, so every wave reaches every barrier (rows past the end are clamped
+  // and not stored)
+  uint32_t rbase = blockIdx.x * R;
+  if (rbase > last) return;  // uniform over the workgroup
+  auto row_ptr = [&](uint32_t rb) {
+    const uint32_t r = rb + slot;
+    return xcol + (uint64_t)(r < last ? r : last) * ldx;
+  };
+  Raw<DT> ring = load_raw<DT>(row_ptr(rbase));
+
+  // per-lane constants: shear coefficients, the modulated diagonal e and c = T_b shift
+  // (rebuilt from the factors whenever the lane's row moves to another sample)
+  BlockConsts k;
+  float cvec[kBlk];
+  uint64_t cur_g = ~0ull;
+  auto set_sample = [&](uint64_t g) {
+    make_consts<false>(load_params(params, bb), k);
+    if (MOD) {
+      const float4* sc4 = reinterpret_cast<const float4*>(scale + g * d + (uint64_t)bb * kBlk);
+      const float4* sh4 = reinterpret_cast<const float4*>(shift + g * d + (uint64_t)bb * kBlk);
 #pragma unroll
-        for (int k = 0; k < kBlk / 4; ++k) {
-          const float4 a = sc4[k], o = sh4[k];
-          const float av[4] = {a.x, a.y, a.z, a.w}, ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float hn = (v[4 * k + j] - mean) * rstd;
-            v[4 * k + j] = __builtin_fmaf(hn, 1.0f + av[j], ov[j]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < kBlk; ++i) v[i] = (v[i] - mean) * rstd;
+      for (int j = 0; j < kBlk / 4; ++j) {
+        const float4 o = sh4[j];
+        cvec[4 * j + 0] = o.x;
+        cvec[4 * j + 1] = o.y;
+        cvec[4 * j + 2] = o.z;
+        cvec[4 * j + 3] = o.w;
       }
-      transform<false>(v, c);
+      transform<false>(cvec, k);  // c = T_b shift, with the unmodulated diagonal
+#pragma unroll
+      for (int j = 0; j < kBlk / 4; ++j) {
+        const float4 a = sc4[j];
+        k.d[4 * j + 0] *= 1.0f + a.x;
+        k.d[4 * j + 1] *= 1.0f + a.y;
+        k.d[4 * j + 2] *= 1.0f + a.z;
+        k.d[4 * j + 3] *= 1.0f + a.w;
+      }
+    }
+    cur_g = g;
+  };
+
+  int buf = 0;
+  for (;;) {
+    const uint32_t r = rbase + slot;
+    const bool store = active && r <= last;
+    const uint32_t rr = r < last ? r : last;
+    // constants first, while only the prefetched row is live
+    const uint64_t g = MOD ? rr / rows_per_sample : 0;
+    if (g != cur_g) set_sample(g);
+    float v[kBlk];
+    unpack(ring, v);
+    const uint32_t rnext = rbase + rstep;
+    ring = load_raw<DT>(row_ptr(rnext <= last ? rnext : rbase));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // row statistics: lanes, then the row's half waves (fixed order)
+    Moments m = block_moments(v);
+    if (!active) m = {0.0f, 0.0f, 0.0f};
+    m = half_merge(m);
+    if (H > 1) {
+      if ((threadIdx.x & 31u) == 0) {
+        part[buf][half][0] = m.n;
+        part[buf][half][1] = m.mean;
+        part[buf][half][2] = m.m2;
+      }
+      __syncthreads();
+      const uint32_t h0 = slot * H;
+      m = {part[buf][h0][0], part[buf][h0][1], part[buf][h0][2]};
+      for (uint32_t i = h0 + 1; i < h0 + H; ++i)
+        m = merge(m, Moments{part[buf][i][0], part[buf][i][1], part[buf][i][2]});
+      buf ^= 1;
+    }
+    const float mean = m.mean;
+    const float rstd = __builtin_amdgcn_rsqf(m.m2 * inv_d + eps);
+
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i) v[i] = (v[i] - mean) * k.d[i];
+    shears<false>(v, k);
+    if (MOD) {
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) v[i] = __builtin_fmaf(rstd, v[i], cvec[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) v[i] *= rstd;
+    }
+    if (store) {
       if (WRITE_Y)
         store_y(reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(y) + (uint64_t)r * ldy) + b * kBlk, v);
       encode_store(v, q + (uint64_t)r * ldq + b * (kBlk / 2), s + (uint64_t)r * lds + b);
     }
+    if (rnext > last) return;  // uniform over the workgroup
+    rbase = rnext;
   }
 }
 
 template <int DT, bool MOD, bool WRITE_Y>
 hipError_t launch_t(const NormArgs& n) {
   const LaunchArgs& a = n.a;
-  const int64_t waves_per_wg = kThreads / 64;
-  int64_t grid = (int64_t)a.cus * kNormBlocksPerCU;
-  const int64_t need = (a.rows + waves_per_wg - 1) / waves_per_wg;
-  if (grid > need) grid = need;
+  const int64_t H = (a.nb + 31) / 32;
+  int64_t R = 256 / (32 * H);
+  if (R < 1) R = 1;
+  const int64_t threads = (32 * H * R + 63) / 64 * 64;
+  // about 12 resident waves per compute unit
+  int64_t per_cu = 12 / (threads / 64);
+  if (per_cu < 1) per_cu = 1;
+  int64_t grid = (int64_t)a.cus * per_cu;
+  const int64_t groups = (a.rows + R - 1) / R;
+  if (grid > groups) grid = groups;
   const int64_t esz = DT == DT_BF16 ? 2 : 4;
-  hipLaunchKernelGGL((norm_kernel<DT, MOD, WRITE_Y>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     (hipStream_t)a.stream, (const uint8_t*)a.x, (uint32_t)a.rows, (uint32_t)a.nb,
-                     (uint32_t)(a.ldx * esz), n.shift, n.scale, (uint32_t)n.rows_per_sample, n.eps,
-                     (float)(1.0 / (double)a.d), (const float*)a.t, a.q, (uint32_t)a.ldq, a.s,
-                     (uint32_t)a.lds, a.y, (uint32_t)(a.ldy * 4));
+  hipLaunchKernelGGL((norm_kernel<DT, MOD, WRITE_Y>), dim3((unsigned)grid), dim3((unsigned)threads),
+                     0, (hipStream_t)a.stream, (const uint8_t*)a.x, (uint32_t)a.rows,
+                     (uint32_t)a.nb, (uint32_t)(a.ldx * esz), n.shift, n.scale,
+                     (uint32_t)n.rows_per_sample, n.eps, (float)(1.0 / (double)a.d),
+                     (const float*)a.t, a.q, (uint32_t)a.ldq, a.s, (uint32_t)a.lds, a.y,
+                     (uint32_t)(a.ldy * 4), (uint32_t)H, (uint32_t)R);
   return hipGetLastError();
 }
 

@@ -147,6 +147,7 @@ def test_norm_validation(L):
     assert norm(p=T + 2) == ALIGN
     assert norm(dtype=9) == DTYPE
     assert norm(d=48, ldx=48) == SHAPE
+    assert norm(d=16416, ldx=16416, q=Q, ldq=8208, lds=513) == SHAPE  # wider than one workgroup
     assert norm(x=None, rows=0, p=None, q=None, s=None) == OK
     assert L.kq_norm_debug(X, 0, 4, 64, 64, None, None, 4, 1e-6, T, Q, 32, S, 2, None, 64, None) == NULL
     assert L.kq_status_string(-8) == b"scalar argument out of range"

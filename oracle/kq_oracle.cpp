@@ -209,6 +209,21 @@ double oq_e2m1_value(int code, int e) {
   return (code & 8) ? -mag : mag;
 }
 
+int oq_dequantize(const uint8_t* q, int64_t ldq, const uint8_t* s, int64_t lds, int64_t rows,
+                  int64_t d, double* out) {
+  if (rows == 0 && d > 0 && d % kBlk == 0) return 0;
+  if (!q || !s || !out || rows < 0 || d <= 0 || d % kBlk != 0 || ldq < d / 2 || lds < d / kBlk)
+    return -1;
+  for (int64_t t = 0; t < rows; ++t)
+    for (int64_t c = 0; c < d; ++c) {
+      const int S = s[t * lds + c / kBlk];
+      const uint8_t byte = q[t * ldq + c / 2];
+      const int code = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+      out[t * d + c] = S == 0xFF ? std::nan("") : oq_e2m1_value(code, S - 127);
+    }
+  return 0;
+}
+
 int oq_encode(const double* y, int64_t rows, int64_t d, uint8_t* q, int64_t ldq,
               uint8_t* s, int64_t lds) {
   if (rows == 0 && d > 0 && d % kBlk == 0) return 0;

@@ -132,6 +132,11 @@ int oq_norm_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t 
                      const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
                      double* h_out, double* y_out, int nthreads);
 
+/* Decode MXFP4 rows back to values: out[t][c] = E2M1(code) * 2^(S - 127) with the
+ * block's E8M0 byte S (0xFF, the NaN scale, decodes to NaN).  [MX] */
+int oq_dequantize(const uint8_t* q, int64_t ldq, const uint8_t* s, int64_t lds, int64_t rows,
+                  int64_t d, double* out);
+
 /* Parity accounting of candidate outputs against the oracle's fp64 values y_o.
  * Per block the tolerance is tol_coef * max|x_blk| (tol_mode 0, the fp32 rule) or
  * tol_coef * max|y_o_blk| (tol_mode 1, the block-relative bf16 rule).

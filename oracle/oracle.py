@@ -61,6 +61,7 @@ def lib():
         L.oq_hadamard_quantize.argtypes = [P, I, I64, I64, I64, P, I64, P, I64, P, I]
         L.oq_norm_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, ctypes.c_double, P, P, I64, P, I64,
                                        P, P, I]
+        L.oq_dequantize.argtypes = [P, I64, P, I64, I64, I64, P]
         L.oq_weight_transform.argtypes = [P, I, I64, I64, I64, P, P]
         L.oq_quantize_weights.argtypes = [P, I, I64, I64, I64, P, P, I64, P, I64, P, I]
         L.oq_classify.argtypes = [P, I, I64, I64, I64, P, I, D, P, I64, P, I64, P, I64, P]
@@ -224,6 +225,28 @@ def norm_quantize(x: np.ndarray, params: np.ndarray, shift=None, scale=None, row
                                 d // 2, _ptr(s), d // 32, _ptr(h), _ptr(y) if want_y else None, nthreads)
     _check(rc, "norm_quantize")
     return q, s, h, y
+
+
+def dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """fp64 values of MXFP4 rows (q [rows, d/2], s [rows, d/32])."""
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.uint8)
+    rows, d = q.shape[0], q.shape[1] * 2
+    out = np.zeros((rows, d), np.float64)
+    _check(lib().oq_dequantize(_ptr(q), q.shape[1], _ptr(s), s.shape[1], rows, d, _ptr(out)), "dequantize")
+    return out
+
+
+def mx_gemm(qa, sa, qb, sb, rows=None, cols=None):
+    """Reference W4A4 product: Y[i][j] = sum_c deq(A)[i][c] * deq(B)[j][c] over the selected
+    rows of A and rows of B (all when None), with the sum of |terms| beside it (the
+    scale of the fp32 accumulation error).  Every product of two decoded MXFP4 values
+    is exact in fp64; the fp64 sum's rounding is far below any fp32 tolerance."""
+    ia = slice(None) if rows is None else np.asarray(rows)
+    ib = slice(None) if cols is None else np.asarray(cols)
+    A = dequantize(np.ascontiguousarray(qa[ia]), np.ascontiguousarray(sa[ia]))
+    B = dequantize(np.ascontiguousarray(qb[ib]), np.ascontiguousarray(sb[ib]))
+    return A @ B.T, np.abs(A) @ np.abs(B).T
 
 
 def weight_transform(w: np.ndarray, params: np.ndarray) -> np.ndarray:

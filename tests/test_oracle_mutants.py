@@ -70,6 +70,12 @@ MUTANTS = {
     "norm_sample_index_modulo": (
         "const int64_t g = row / rows_per_sample;",
         "const int64_t g = row % rows_per_sample;"),
+    "dequant_nibbles_swapped": (
+        "const int code = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);",
+        "const int code = (c % 2 == 0) ? (byte >> 4) : (byte & 0xF);"),
+    "dequant_scale_bias": (
+        "out[t * d + c] = S == 0xFF ? std::nan(\"\") : oq_e2m1_value(code, S - 127);",
+        "out[t * d + c] = S == 0xFF ? std::nan(\"\") : oq_e2m1_value(code, S - 128);"),
     "amax_without_abs": (
         "        amax = std::max(amax, std::fabs(yb[i]));\n      }\n      uint8_t* qb",
         "        amax = std::max(amax, yb[i]);\n      }\n      uint8_t* qb"),

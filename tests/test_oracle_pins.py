@@ -419,3 +419,51 @@ def test_norm_shift_invariance_and_modulation_per_sample(oq):
     T = oq.expand(p)
     ref = np.einsum("bij,rbj->rbi", T, hm.reshape(7, 2, 32)).reshape(7, 64)
     np.testing.assert_allclose(ym, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+# ------------------------------------------------------------------ W4A4 product
+
+def test_dequantize_table_and_round_trip(oq):
+    # every code at a few scales against the E2M1 table of the OCP MX spec
+    table = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    q = np.zeros((3, 16), np.uint8)
+    for i in range(16):
+        q[:, i // 2] |= np.uint8(i << (4 * (i % 2)))  # code i at channel i
+    q[:, 8:] = q[:, :8]
+    s = np.array([[127], [130], [120]], np.uint8)
+    v = oq.dequantize(q, s)
+    for r, e in enumerate([0, 3, -7]):
+        for c in range(32):
+            code = c % 16
+            mag = table[code & 7] * 2.0 ** e
+            assert v[r, c] == (-mag if code & 8 else mag)
+    # blocks whose largest code is 6 (value 4) or 7 (value 6) re-encode to themselves
+    rng = np.random.default_rng(61)
+    codes = rng.integers(0, 16, size=(20, 64)).astype(np.uint8)
+    codes[:, ::32] = 7
+    qq = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    ss = rng.integers(100, 150, size=(20, 2)).astype(np.uint8)
+    q2, s2 = oq.encode(oq.dequantize(qq, ss))
+    assert np.array_equal(q2, qq) and np.array_equal(s2, ss)
+
+
+def test_mx_gemm_on_grid_values_is_the_plain_product(oq):
+    # values already on the MXFP4 grid survive quantization exactly, so the W4A4 product
+    # of their encodings equals numpy's product of the original values
+    rng = np.random.default_rng(62)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+
+    def on_grid(rows, d):
+        v = rng.choice(grid, size=(rows, d)) * rng.choice([-1, 1], size=(rows, d))
+        v[:, ::32] = 6.0  # every block's amax is 6: scale 2^0 ... then scaled per block
+        e = rng.integers(-4, 5, size=(rows, d // 32))
+        return v * np.repeat(2.0 ** e, 32, axis=1)
+
+    a, b = on_grid(9, 128), on_grid(7, 128)
+    qa, sa = oq.encode(a)
+    qb, sb = oq.encode(b)
+    Y, Yabs = oq.mx_gemm(qa, sa, qb, sb)
+    assert np.array_equal(Y, a @ b.T)
+    assert np.array_equal(Yabs, np.abs(a) @ np.abs(b).T)
+    Ysub, _ = oq.mx_gemm(qa, sa, qb, sb, rows=[8, 0], cols=[3])
+    assert np.array_equal(Ysub[:, 0], (a @ b.T)[[8, 0], 3])

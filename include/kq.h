@@ -205,6 +205,22 @@ int kq_norm_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx
                   const float* params, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, float* y,
                   int64_t ldy, void* stream);
 
+/* The W4A4 product that consumes the quantizer's outputs (KroQuant abstract:
+ * W4A4 with MXFP4 activations; the transform's inverse sits in the weights):
+ *   out[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k],   deq = E2M1(code) * 2^(S - 127)
+ * A: activations as kq_quantize / kq_norm_quantize write them, qa uint8 [M][lda]
+ *    codes (lda >= K/2 bytes) and sa uint8 [M][ldsa] E8M0 scales (ldsa >= K/32);
+ * B: weights as kq_quantize_weights writes them, qb [N][ldb], sb [N][ldsb].
+ * out: [M][ldo] (ldo >= N elements) of out_dtype KQ_FP32 or KQ_BF16 (round to
+ * nearest even from the fp32 accumulation).  K: multiple of 32.  qa, qb and their
+ * pitches 16-byte aligned.  Runs on the gfx950 scaled matrix cores
+ * (fp4 x fp4 with per-32 E8M0 scales, fp32 accumulation); scale bytes 0xFF (NaN)
+ * give unspecified results.
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_DTYPE, KQ_ERR_HIP. */
+int kq_mx_gemm(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
+               const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+               int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream);
+
 /* Static text for a kq_status value (never NULL). */
 const char* kq_status_string(int status);
 

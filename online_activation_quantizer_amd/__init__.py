@@ -8,5 +8,5 @@ from .kq import (  # noqa: F401
     KQ_AUTO, KQ_BF16, KQ_BUTTERFLY, KQ_FP32, KQ_MFMA, KQ_T_DENSE_BF16X3, KQ_T_DENSE_F32,
     KQ_T_PARAMS, KQError, STATUS, kq_expand_factors, kq_quantize, kq_transform_debug, lib,
     sq_quantize, sq_transform_debug, expanded_numel, EXPORTED_SYMBOLS, kq_quantize_weights,
-    kq_weights_debug, hq_quantize, hq_transform_debug, kq_norm_quantize, kq_norm_debug,
+    kq_weights_debug, hq_quantize, hq_transform_debug, kq_norm_quantize, kq_norm_debug, kq_mx_gemm,
 )

@@ -282,6 +282,27 @@ int kq_norm_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx
                    lds, y, ldy, true, stream);
 }
 
+int kq_mx_gemm(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
+               const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+               int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream) {
+  if (out_dtype != KQ_FP32 && out_dtype != KQ_BF16) return KQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || K / 32 > kMaxBlocks || M > kMaxRows ||
+      N > kMaxRows || lda < K / 2 || ldb < K / 2 || ldsa < K / 32 || ldsb < K / 32 || ldo < N ||
+      lda > kMaxPitch || ldb > kMaxPitch || ldsa > kMaxPitch || ldsb > kMaxPitch ||
+      ldo * (out_dtype == KQ_FP32 ? 4 : 2) > kMaxPitch)
+    return KQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return KQ_OK;
+  if (((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return KQ_ERR_SHAPE;
+  if (!qa || !sa || !qb || !sb || !out) return KQ_ERR_NULL;
+  if (!aligned(qa, 16) || !aligned(qb, 16) || lda % 16 != 0 || ldb % 16 != 0 ||
+      !aligned(out, out_dtype == KQ_FP32 ? 4 : 2))
+    return KQ_ERR_ALIGN;
+  const kq::GemmArgs g{qa, lda, sa, ldsa, qb, ldb, sb, ldsb, M, N, K, out, ldo,
+                       out_dtype == KQ_BF16, stream};
+  const hipError_t e = kq::launch_mx_gemm(g);
+  return e == hipSuccess ? KQ_OK : fail_hip(e);
+}
+
 const char* kq_status_string(int status) {
   switch (status) {
     case KQ_OK: return "ok";

@@ -1,0 +1,191 @@
+// kq_gemm.hip — the W4A4 product that consumes the quantizer's output (gfx950).
+//
+//   Y[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k]
+//
+// A = the activations' MXFP4 codes and E8M0 scales exactly as kq_quantize writes
+// them ([M][K/2] code bytes, [M][K/32] scale bytes), B = the weights' (as
+// kq_quantize_weights writes them, [N][K/2] and [N][K/32]).  KroQuant abstract:
+// W4A4 with MXFP4 activations and weights; the transform's inverse folded into the
+// weights makes this product equal W x up to the two quantizations.
+//
+// Matrix cores.  v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in fp4
+// (E2M1) multiplies a 32x64 by a 64x32 tile and applies one E8M0 scale per 32
+// K-values of each row (OCP MX block size) in hardware, accumulating in fp32.  Lane
+// l supplies row l % 32 and the 32 K-values 32 (l / 32) .. + 31 as 16 bytes, low
+// nibble first, which is exactly one 32-element block of the quantizer's layout,
+// plus that block's scale byte (chosen from a 32-bit register by op_sel).
+//
+// Tiling.  A workgroup (4 waves, 2 x 2) computes a 128 x 128 tile of Y; each wave a
+// 64 x 64 quarter as 2 x 2 MFMA tiles.  K advances 128 at a time: the 128 x 64-byte
+// code tiles of A and B and their 128 x 4 scale bytes are staged through LDS
+// (double-buffered, code rows padded to 80 bytes against bank conflicts), the next
+// step's global loads in flight during this step's MFMAs.  Rows past M or N are
+// clamped on load and not stored; K-blocks past K load as code 0 with scale 2^0
+// (value 0).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kq_launch.hpp"
+
+namespace kq {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128, kBN = 128;
+constexpr int kBKBytes = 64;               // K = 128 fp4 values per step
+constexpr int kPitch = kBKBytes + 16;      // LDS code-row pitch
+constexpr int kTileCodes = 128 * kPitch;   // bytes per operand per stage
+constexpr uint32_t kScaleOne = 0x7F7F7F7Fu;  // four E8M0 bytes of 2^0
+
+struct Stage {
+  uint4 a[2], b[2];  // this thread's two 16-byte code chunks of A and of B
+  uint32_t sc;       // one row's 4 scale bytes (threads 0-127: A, 128-255: B)
+};
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void mx_gemm_kernel(
+    const uint8_t* __restrict__ qa, uint32_t lda, const uint8_t* __restrict__ sa, uint32_t ldsa,
+    const uint8_t* __restrict__ qb, uint32_t ldb, const uint8_t* __restrict__ sb, uint32_t ldsb,
+    uint32_t M, uint32_t N, uint32_t K, void* __restrict__ out, uint32_t ldo, uint32_t tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint8_t codes[2][2][kTileCodes];  // [stage][A/B]
+  __shared__ uint32_t scales[2][2][128];
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t wm = wave >> 1, wn = wave & 1u;
+  const uint32_t tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const uint32_t m0 = tm * kBM, n0 = tn * kBN;
+  const uint32_t kbytes = K / 2, kblocks = K / 32;
+  const uint32_t nsteps = (K + 127) / 128;
+
+  // global -> register loads of one K step
+  auto load_stage = [&](uint32_t step, Stage& st) {
+    const uint32_t kb0 = step * kBKBytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t c = tid + 256u * i;       // chunk: row c / 4, 16-byte column c % 4
+      const uint32_t row = c >> 2, col = (c & 3u) * 16u;
+      const bool kin = kb0 + col < kbytes;
+      const uint32_t ra = m0 + row < M ? m0 + row : M - 1;
+      const uint32_t rb = n0 + row < N ? n0 + row : N - 1;
+      const uint4 za = kin ? *reinterpret_cast<const uint4*>(qa + (uint64_t)ra * lda + kb0 + col)
+                           : make_uint4(0, 0, 0, 0);
+      const uint4 zb = kin ? *reinterpret_cast<const uint4*>(qb + (uint64_t)rb * ldb + kb0 + col)
+                           : make_uint4(0, 0, 0, 0);
+      st.a[i] = za;
+      st.b[i] = zb;
+    }
+    // scales: thread t < 128 takes A row t, t >= 128 takes B row t - 128
+    const bool isb = tid >= 128u;
+    const uint32_t row = tid & 127u;
+    const uint32_t r = isb ? (n0 + row < N ? n0 + row : N - 1) : (m0 + row < M ? m0 + row : M - 1);
+    const uint8_t* srow = (isb ? sb + (uint64_t)r * ldsb : sa + (uint64_t)r * ldsa) + step * 4u;
+    uint32_t w = kScaleOne;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (step * 4u + j < kblocks) w = (w & ~(0xFFu << (8 * j))) | ((uint32_t)srow[j] << (8 * j));
+    st.sc = w;
+  };
+  auto store_stage = [&](int buf, const Stage& st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t c = tid + 256u * i;
+      const uint32_t off = (c >> 2) * kPitch + (c & 3u) * 16u;
+      *reinterpret_cast<uint4*>(&codes[buf][0][off]) = st.a[i];
+      *reinterpret_cast<uint4*>(&codes[buf][1][off]) = st.b[i];
+    }
+    scales[buf][tid >> 7][tid & 127u] = st.sc;
+  };
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+
+  const uint32_t lr = lane & 31u, h = lane >> 5;
+  Stage st;
+  load_stage(0, st);
+  store_stage(0, st);
+  __syncthreads();
+  int buf = 0;
+  for (uint32_t step = 0; step < nsteps; ++step) {
+    const bool more = step + 1 < nsteps;
+    if (more) load_stage(step + 1, st);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v8i A[2], B[2];
+      uint32_t sA[2], sB[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t ra = wm * 64u + 32u * i + lr, rb = wn * 64u + 32u * i + lr;
+        const uint4 va = *reinterpret_cast<const uint4*>(&codes[buf][0][ra * kPitch + 32u * ks + 16u * h]);
+        const uint4 vb = *reinterpret_cast<const uint4*>(&codes[buf][1][rb * kPitch + 32u * ks + 16u * h]);
+        A[i] = v8i{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
+        B[i] = v8i{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
+        // the lane's block scale moved to byte 2 ks (op_sel picks it)
+        sA[i] = scales[buf][0][ra] >> (8u * h);
+        sB[i] = scales[buf][1][rb] >> (8u * h);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (ks == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                A[i], B[j], acc[i][j], 4, 4, 0, (int)sA[i], 0, (int)sB[j]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                A[i], B[j], acc[i][j], 4, 4, 2, (int)sA[i], 2, (int)sB[j]);
+        }
+    }
+    if (more) {
+      store_stage(buf ^ 1, st);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  // acc[i][j][r]: row 8 (r / 4) + 4 h + r % 4 of MFMA tile (i, j), column lr
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t col = n0 + wn * 64u + 32u * j + lr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t row = m0 + wm * 64u + 32u * i + 8u * (r >> 2) + 4u * h + (r & 3);
+        if (row >= M) continue;
+        if (OUT_BF16) {
+          const float v = acc[i][j][r];
+          // round to nearest even (finite values)
+          const uint32_t u = __float_as_uint(v);
+          const uint16_t hb = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+          reinterpret_cast<uint16_t*>(out)[(uint64_t)row * ldo + col] = hb;
+        } else {
+          reinterpret_cast<float*>(out)[(uint64_t)row * ldo + col] = acc[i][j][r];
+        }
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mx_gemm(const GemmArgs& g) {
+  const int64_t tiles_m = (g.M + kBM - 1) / kBM, tiles_n = (g.N + kBN - 1) / kBN;
+  const int64_t grid = tiles_m * tiles_n;
+  if (g.out_bf16)
+    hipLaunchKernelGGL(mx_gemm_kernel<true>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)g.stream,
+                       g.qa, (uint32_t)g.lda, g.sa, (uint32_t)g.ldsa, g.qb, (uint32_t)g.ldb, g.sb,
+                       (uint32_t)g.ldsb, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K, g.out,
+                       (uint32_t)g.ldo, (uint32_t)tiles_n);
+  else
+    hipLaunchKernelGGL(mx_gemm_kernel<false>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)g.stream,
+                       g.qa, (uint32_t)g.lda, g.sa, (uint32_t)g.ldsa, g.qb, (uint32_t)g.ldb, g.sb,
+                       (uint32_t)g.ldsb, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K, g.out,
+                       (uint32_t)g.ldo, (uint32_t)tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace kq

@@ -44,6 +44,23 @@ struct NormArgs {
 // Resident-grid target of the row-per-wave normalization kernel.
 constexpr int kNormBlocksPerCU = 4;
 
+// W4A4 product of two MXFP4 operands (codes + E8M0 scales, K along rows).
+struct GemmArgs {
+  const uint8_t* qa;
+  int64_t lda;   // bytes
+  const uint8_t* sa;
+  int64_t ldsa;  // bytes
+  const uint8_t* qb;
+  int64_t ldb;
+  const uint8_t* sb;
+  int64_t ldsb;
+  int64_t M, N, K;
+  void* out;     // [M][ldo] float32 or bf16
+  int64_t ldo;   // elements
+  bool out_bf16;
+  void* stream;
+};
+
 inline int64_t gcd64(int64_t a, int64_t b) {
   while (b) {
     const int64_t r = a % b;
@@ -73,6 +90,7 @@ hipError_t launch_butterfly(const LaunchArgs& a);
 hipError_t launch_weights(const LaunchArgs& a);   // W T^-1 along each row, then MXFP4
 hipError_t launch_hadamard(const LaunchArgs& a);  // fixed block-Hadamard, then MXFP4
 hipError_t launch_norm(const NormArgs& n);        // LayerNorm + modulation, T_b, MXFP4
+hipError_t launch_mx_gemm(const GemmArgs& g);    // Y = deq(A) deq(B)^T on scaled MFMA
 hipError_t launch_sq(const LaunchArgs& a);
 hipError_t launch_mfma(const LaunchArgs& a);
 hipError_t launch_expand(const float* params, int64_t nb, int tfmt, void* out, void* stream);

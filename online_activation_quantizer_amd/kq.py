@@ -25,7 +25,7 @@ KQ_AUTO, KQ_BUTTERFLY, KQ_MFMA = 0, 1, 2
 EXPORTED_SYMBOLS = ("kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
                     "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug",
                     "hq_quantize", "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug",
-                    "kq_status_string", "kq_last_hip_error")
+                    "kq_mx_gemm", "kq_status_string", "kq_last_hip_error")
 
 
 class KQError(RuntimeError):
@@ -60,6 +60,7 @@ def lib():
         F = ctypes.c_float
         L.kq_norm_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, F, P, P, I64, P, I64, P]
         L.kq_norm_debug.argtypes = [P, I, I64, I64, I64, P, P, I64, F, P, P, I64, P, I64, P, I64, P]
+        L.kq_mx_gemm.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, I64, I, P]
         L.kq_status_string.argtypes = [I]
         L.kq_status_string.restype = ctypes.c_char_p
         L.kq_last_hip_error.argtypes = []
@@ -250,3 +251,19 @@ def kq_norm_debug(x, params, shift=None, scale=None, rows_per_sample=None, eps: 
                                _row_pitch(q), s.data_ptr(), _row_pitch(s), y.data_ptr(), _row_pitch(y),
                                _stream(stream)), "kq_norm_debug")
     return q, s, y
+
+
+def kq_mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
+    """W4A4 product out[m][n] = sum_k deq(A)[m][k] deq(B)[n][k] of two MXFP4 operands
+    (codes [rows, K/2], scales [rows, K/32]); out float32 (default) or bfloat16."""
+    import torch
+    M, N, K = qa.shape[0], qb.shape[0], qa.shape[1] * 2
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=qa.device)
+    code = {torch.float32: KQ_FP32, torch.bfloat16: KQ_BF16}.get(out.dtype)
+    if code is None:
+        raise KQError(KQ_ERR_DTYPE, f"unsupported output dtype {out.dtype}")
+    _check(lib().kq_mx_gemm(qa.data_ptr(), _row_pitch(qa), sa.data_ptr(), _row_pitch(sa), qb.data_ptr(),
+                            _row_pitch(qb), sb.data_ptr(), _row_pitch(sb), M, N, K, out.data_ptr(),
+                            _row_pitch(out), code, _stream(stream)), "kq_mx_gemm")
+    return out

@@ -28,8 +28,8 @@ def test_header_symbols_exported(L):
     names = header_functions()
     assert {"kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
             "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug", "hq_quantize",
-            "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug", "kq_status_string",
-            "kq_last_hip_error"} <= set(names)
+            "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug", "kq_mx_gemm",
+            "kq_status_string", "kq_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -151,6 +151,25 @@ def test_norm_validation(L):
     assert norm(x=None, rows=0, p=None, q=None, s=None) == OK
     assert L.kq_norm_debug(X, 0, 4, 64, 64, None, None, 4, 1e-6, T, Q, 32, S, 2, None, 64, None) == NULL
     assert L.kq_status_string(-8) == b"scalar argument out of range"
+
+
+def test_mx_gemm_validation(L):
+    def g(qa=Q, lda=64, sa=S, ldsa=4, qb=T, ldb=64, sb=Y, ldsb=4, M=8, N=8, K=128, out=X, ldo=8, dt=1):
+        return L.kq_mx_gemm(qa, lda, sa, ldsa, qb, ldb, sb, ldsb, M, N, K, out, ldo, dt, None)
+    assert g(dt=5) == DTYPE
+    assert g(K=48, lda=32, ldb=32) == SHAPE     # K not a multiple of 32
+    assert g(K=0) == SHAPE
+    assert g(lda=32) == SHAPE                    # pitch below K/2
+    assert g(ldsa=3) == SHAPE
+    assert g(ldo=7) == SHAPE
+    assert g(M=-1) == SHAPE
+    assert g(qa=None) == NULL
+    assert g(sb=None) == NULL
+    assert g(out=None) == NULL
+    assert g(qa=Q + 8) == ALIGN
+    assert g(lda=72) == ALIGN
+    assert g(out=X + 2) == ALIGN                 # fp32 output needs 4 bytes
+    assert g(M=0, qa=None, sa=None, qb=None, sb=None, out=None) == OK
 
 
 def test_expand_validation(L):

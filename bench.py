@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--no-sq", action="store_true",
                     help="skip the SmoothQuant and block-Hadamard comparison timings")
     ap.add_argument("--no-weights", action="store_true", help="skip the weight-side timing")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the W4A4 product timing")
     ap.add_argument("--no-norm", action="store_true",
                     help="skip the normalization-fused quantizer timing")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -203,6 +204,37 @@ def norm_timing(args, cfg, xs, ps, qs, ss, kq_ms):
             "fused_over_quantizer_alone": round(f_ms / kq_ms, 4)}
 
 
+PEAK_FP4_TFLOPS = 10100.0  # dense fp4 matrix-core peak of one MI355X
+
+
+def gemm_timing(args, qs, ss):
+    """The W4A4 product consuming the quantizer's output: FLUX.1-schnell MLP
+    up-projection, Y[4608, 12288] = deq(Qx)[4608, 3072] deq(Qw)[12288, 3072]^T, with
+    the activation codes of the pool's first set and quantized weights, bf16 out."""
+    import torch
+
+    import synth
+    import online_activation_quantizer_amd as kq
+    wcfg = synth.get_weight_config("flux_w_mlp")
+    w, p = synth.make_weights(wcfg)
+    qw, sw = kq.kq_quantize_weights(torch.from_numpy(w.view(np.int16)).cuda(), torch.from_numpy(p).cuda())
+    M, N, K = qs[0].shape[0], wcfg.rows, wcfg.d
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    P = len(qs)
+
+    def step(i):
+        j = i % P
+        kq.kq_mx_gemm(qs[j], ss[j], qw, sw, out=out)
+
+    steps = max(8, args.steps // 10)
+    ms = (timed(step, steps, args.warmup, torch.cuda.current_stream()) if args.eager
+          else timed_graph(step, steps, min(args.warmup, 10)))
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return {"workload": f"FLUX.1-schnell MLP up-projection {M}x{N}x{K}, fp4 x fp4 (MXFP4), bf16 out",
+            "ms_per_call": round(ms, 6), "tflops": round(tflops, 1),
+            "mfma_frac_fp4": round(tflops / PEAK_FP4_TFLOPS, 4)}
+
+
 def weights_timing(args):
     """The weight side (W T^-1 then MXFP4 along the input channels) on the FLUX MLP
     up-projection W[12288, 3072] bf16, timed like the activation step over 4
@@ -299,6 +331,7 @@ def main():
 
     weights = None if args.no_weights else weights_timing(args)
     norm = None if args.no_norm else norm_timing(args, cfg, xs, ps, qs, ss, ms)
+    gemm = None if args.no_gemm else gemm_timing(args, qs, ss)
     ceiling = None if args.no_ceiling else stream_ceiling(args, xs, qs, ss, ms)
 
     # parity of one production step against the oracle
@@ -353,6 +386,8 @@ def main():
         out["weights"] = weights
     if norm is not None:
         out["norm_fused"] = norm
+    if gemm is not None:
+        out["w4a4_gemm"] = gemm
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

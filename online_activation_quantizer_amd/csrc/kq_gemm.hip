@@ -18,8 +18,8 @@
 // Tiling.  A workgroup (4 waves, 2 x 2) computes a 128 x 128 tile of Y; each wave a
 // 64 x 64 quarter as 2 x 2 MFMA tiles.  K advances 128 at a time: the 128 x 64-byte
 // code tiles of A and B and their 128 x 4 scale bytes are staged through LDS
-// (double-buffered, code rows padded to 80 bytes against bank conflicts), the next
-// step's global loads in flight during this step's MFMAs.  Rows past M or N are
+// (double-buffered, code rows padded to 80 bytes against bank conflicts), with the
+// global loads of the step after next in flight during this step's MFMAs.  Rows past M or N are
 // clamped on load and not stored; K-blocks past K load as code 0 with scale 2^0
 // (value 0).
 #include <hip/hip_runtime.h>
@@ -44,16 +44,29 @@ struct Stage {
   uint32_t sc;       // one row's 4 scale bytes (threads 0-127: A, 128-255: B)
 };
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool SCALE_WORDS>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(
     const uint8_t* __restrict__ qa, uint32_t lda, const uint8_t* __restrict__ sa, uint32_t ldsa,
     const uint8_t* __restrict__ qb, uint32_t ldb, const uint8_t* __restrict__ sb, uint32_t ldsb,
-    uint32_t M, uint32_t N, uint32_t K, void* __restrict__ out, uint32_t ldo, uint32_t tiles_n) {
+    uint32_t M, uint32_t N, uint32_t K, void* __restrict__ out, uint32_t ldo, uint32_t tiles_n,
+    uint32_t xcd_cols) {
   __shared__ __attribute__((aligned(16))) uint8_t codes[2][2][kTileCodes];  // [stage][A/B]
   __shared__ uint32_t scales[2][2][128];
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t wm = wave >> 1, wn = wave & 1u;
-  const uint32_t tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  // Tile order.  Workgroups go to the 8 XCDs round-robin by index; when xcd_cols > 0
+  // (tiles_n = 8 xcd_cols) XCD x gets the tile columns [x xcd_cols, (x+1) xcd_cols)
+  // for every tile row, so the B tiles it reads stay in its own L2 while the tile
+  // rows advance, and consecutive workgroups on an XCD share their A tile.
+  uint32_t tm, tn;
+  if (xcd_cols) {
+    const uint32_t x = blockIdx.x & 7u, local = blockIdx.x >> 3;
+    tm = local / xcd_cols;
+    tn = x * xcd_cols + (local - tm * xcd_cols);
+  } else {
+    tm = blockIdx.x / tiles_n;
+    tn = blockIdx.x - tm * tiles_n;
+  }
   const uint32_t m0 = tm * kBM, n0 = tn * kBN;
   const uint32_t kbytes = K / 2, kblocks = K / 32;
   const uint32_t nsteps = (K + 127) / 128;
@@ -81,9 +94,13 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
     const uint32_t r = isb ? (n0 + row < N ? n0 + row : N - 1) : (m0 + row < M ? m0 + row : M - 1);
     const uint8_t* srow = (isb ? sb + (uint64_t)r * ldsb : sa + (uint64_t)r * ldsa) + step * 4u;
     uint32_t w = kScaleOne;
+    if (SCALE_WORDS && step * 4u + 4u <= kblocks) {
+      w = *reinterpret_cast<const uint32_t*>(srow);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (step * 4u + j < kblocks) w = (w & ~(0xFFu << (8 * j))) | ((uint32_t)srow[j] << (8 * j));
+      for (int j = 0; j < 4; ++j)
+        if (step * 4u + j < kblocks) w = (w & ~(0xFFu << (8 * j))) | ((uint32_t)srow[j] << (8 * j));
+    }
     st.sc = w;
   };
   auto store_stage = [&](int buf, const Stage& st) {
@@ -104,14 +121,16 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
   const uint32_t lr = lane & 31u, h = lane >> 5;
-  Stage st;
-  load_stage(0, st);
-  store_stage(0, st);
+  // step s is computed from LDS while step s + 1 waits in registers for its LDS
+  // slot and step s + 2 is in flight from memory
+  Stage nxt, far;
+  load_stage(0, nxt);
+  store_stage(0, nxt);
+  if (nsteps > 1) load_stage(1, nxt);
   __syncthreads();
   int buf = 0;
   for (uint32_t step = 0; step < nsteps; ++step) {
-    const bool more = step + 1 < nsteps;
-    if (more) load_stage(step + 1, st);
+    if (step + 2 < nsteps) load_stage(step + 2, far);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       v8i A[2], B[2];
@@ -139,8 +158,10 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
                 A[i], B[j], acc[i][j], 4, 4, 2, (int)sA[i], 2, (int)sB[j]);
         }
     }
-    if (more) {
-      store_stage(buf ^ 1, st);
+    if (step + 1 < nsteps) {
+      // the other slot was last read before the previous barrier
+      store_stage(buf ^ 1, nxt);
+      nxt = far;
       __syncthreads();
       buf ^= 1;
     }
@@ -172,19 +193,28 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
 
 }  // namespace
 
+template <bool OUT_BF16, bool SCALE_WORDS>
+void launch_t(const GemmArgs& g, int64_t grid, int64_t tiles_n, int64_t xcd_cols) {
+  hipLaunchKernelGGL((mx_gemm_kernel<OUT_BF16, SCALE_WORDS>), dim3((unsigned)grid), dim3(256), 0,
+                     (hipStream_t)g.stream, g.qa, (uint32_t)g.lda, g.sa, (uint32_t)g.ldsa, g.qb,
+                     (uint32_t)g.ldb, g.sb, (uint32_t)g.ldsb, (uint32_t)g.M, (uint32_t)g.N,
+                     (uint32_t)g.K, g.out, (uint32_t)g.ldo, (uint32_t)tiles_n, (uint32_t)xcd_cols);
+}
+
 hipError_t launch_mx_gemm(const GemmArgs& g) {
   const int64_t tiles_m = (g.M + kBM - 1) / kBM, tiles_n = (g.N + kBN - 1) / kBN;
   const int64_t grid = tiles_m * tiles_n;
-  if (g.out_bf16)
-    hipLaunchKernelGGL(mx_gemm_kernel<true>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)g.stream,
-                       g.qa, (uint32_t)g.lda, g.sa, (uint32_t)g.ldsa, g.qb, (uint32_t)g.ldb, g.sb,
-                       (uint32_t)g.ldsb, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K, g.out,
-                       (uint32_t)g.ldo, (uint32_t)tiles_n);
-  else
-    hipLaunchKernelGGL(mx_gemm_kernel<false>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)g.stream,
-                       g.qa, (uint32_t)g.lda, g.sa, (uint32_t)g.ldsa, g.qb, (uint32_t)g.ldb, g.sb,
-                       (uint32_t)g.ldsb, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K, g.out,
-                       (uint32_t)g.ldo, (uint32_t)tiles_n);
+  const int64_t xcd_cols = tiles_n % 8 == 0 ? tiles_n / 8 : 0;
+  // whole 32-bit scale words when every scale row starts 4-byte aligned
+  const bool words = ((uintptr_t)g.sa % 4 == 0) && ((uintptr_t)g.sb % 4 == 0) && g.ldsa % 4 == 0 &&
+                     g.ldsb % 4 == 0;
+  if (g.out_bf16) {
+    if (words) launch_t<true, true>(g, grid, tiles_n, xcd_cols);
+    else launch_t<true, false>(g, grid, tiles_n, xcd_cols);
+  } else {
+    if (words) launch_t<false, true>(g, grid, tiles_n, xcd_cols);
+    else launch_t<false, false>(g, grid, tiles_n, xcd_cols);
+  }
   return hipGetLastError();
 }
 

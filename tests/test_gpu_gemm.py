@@ -38,7 +38,8 @@ def check(Y, Yref, Yabs, K, label):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (37, 45, 96), (128, 128, 128), (130, 257, 1152),
-                                   (300, 200, 2240), (64, 512, 3072)])
+                                   (300, 200, 2240), (64, 512, 3072), (300, 1024, 256),
+                                   (129, 2048, 608)])
 def test_mx_gemm_random_codes(M, N, K):
     import torch
     say(f"[mx gemm] {M}x{N}x{K}")

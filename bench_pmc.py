@@ -3,9 +3,9 @@
 the quantizer kernel, calibrated against a plain copy of known size.
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o fetch -- \\
-        python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --eager --calib-copy-mib 256
+        python3 bench.py --steps 8 --warmup 2 --no-cpu --eager --no-gemm --no-ceiling --calib-copy-mib 256
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o write -- \\
-        python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --eager --calib-copy-mib 256
+        python3 bench.py --steps 8 --warmup 2 --no-cpu --eager --no-gemm --no-ceiling --calib-copy-mib 256
     python3 bench_pmc.py DIR 256
 
 FETCH_SIZE / WRITE_SIZE are read in KiB per dispatch.  The copy kernel reads and
@@ -26,18 +26,44 @@ import bench
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
+# kernels whose traffic is summarized: (key, name prefix in the trace, algorithmic
+# read bytes, algorithmic write bytes, what it is)
+FLUX_E = 4608 * 3072
+WEIGHT_E = 12288 * 3072
+KERNELS = [
+    ("kq", "void kq::(anonymous namespace)::butterfly_kernel<0, false, 0>", FLUX_E * 2 + 96 * 60,
+     FLUX_E // 2 + FLUX_E // 32, "kq_quantize (butterfly), 4608x3072 bf16"),
+    ("hq", "void kq::(anonymous namespace)::butterfly_kernel<0, false, 2>", FLUX_E * 2,
+     FLUX_E // 2 + FLUX_E // 32, "hq_quantize (block Hadamard), 4608x3072 bf16"),
+    ("sq", "void kq::(anonymous namespace)::sq_kernel<0, false>", FLUX_E * 2 + 3072 * 4,
+     FLUX_E // 2 + FLUX_E // 32, "sq_quantize (SmoothQuant), 4608x3072 bf16"),
+    ("norm", "void kq::(anonymous namespace)::norm_kernel<0, true, false>", FLUX_E * 2 + 2 * 3072 * 4 + 96 * 60,
+     FLUX_E // 2 + FLUX_E // 32, "kq_norm_quantize (LayerNorm + modulation fused), 4608x3072 bf16"),
+    ("weights", "void kq::(anonymous namespace)::butterfly_kernel<0, false, 1>", WEIGHT_E * 2 + 96 * 60,
+     WEIGHT_E // 2 + WEIGHT_E // 32, "kq_quantize_weights, 12288x3072 bf16"),
+]
+
+
 def per_kernel(csv_path, counter):
-    out = {"kq": [], "copy": []}
+    out = {k[0]: [] for k in KERNELS}
+    out["copy"] = []
     for r in csv.DictReader(open(csv_path)):
         if r["Counter_Name"] != counter:
             continue
         name = r["Kernel_Name"]
         v = float(r["Counter_Value"])
-        if "butterfly_kernel<0, false>" in name:
-            out["kq"].append(v)
-        elif "copy" in name.lower() and "bfloat16" not in name:
-            out["copy"].append(v)
+        for key, prefix, *_ in KERNELS:
+            if name.startswith(prefix):
+                out[key].append(v)
+                break
+        else:
+            if "copy" in name.lower() and "bfloat16" not in name:
+                out["copy"].append(v)
     return out
+
+
+CMD = ("python3 bench.py --steps 8 --warmup 2 --no-cpu --eager --no-gemm --no-ceiling "
+       "--calib-copy-mib %d")
 
 
 def main():
@@ -49,35 +75,46 @@ def main():
     f_copy = max(fetch["copy"]) * 1024.0
     w_copy = max(write["copy"]) * 1024.0
     f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
-    rd = statistics.median(fetch["kq"]) * 1024.0 * f_scale
-    wr = statistics.median(write["kq"]) * 1024.0 * w_scale
-    elems = 4608 * 3072
-    algo_rd, algo_wr = elems * 2 + 96 * 60, elems // 2 + elems // 32
+    rows = {}
+    for key, _, algo_rd, algo_wr, what in KERNELS:
+        if not fetch[key] or not write[key]:
+            continue
+        rd = statistics.median(fetch[key]) * 1024.0 * f_scale
+        wr = statistics.median(write[key]) * 1024.0 * w_scale
+        rows[key] = dict(what=what, fetch_kib=statistics.median(fetch[key]),
+                         write_kib=statistics.median(write[key]), rd=rd, wr=wr, algo_rd=algo_rd,
+                         algo_wr=algo_wr)
+    kq = rows["kq"]
     res = {
         "kernel": "butterfly_kernel<bf16> (kq_quantize, KQ_T_PARAMS), 4608x3072 bf16, 96 factor sets",
         "kernel_source_sha256": bench.kernel_source_hash(),
-        "fetch_size_kib_per_launch": statistics.median(fetch["kq"]),
-        "write_size_kib_per_launch": statistics.median(write["kq"]),
+        "fetch_size_kib_per_launch": kq["fetch_kib"],
+        "write_size_kib_per_launch": kq["write_kib"],
         "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_kib": f_copy / 1024, "write_kib": w_copy / 1024,
                              "fetch_scale": f_scale, "write_scale": w_scale},
-        "read_bytes_per_launch": rd,
-        "write_bytes_per_launch": wr,
-        "traffic_bytes_per_launch": rd + wr,
-        "algorithmic_read_bytes": algo_rd,
-        "algorithmic_write_bytes": algo_wr,
+        "read_bytes_per_launch": kq["rd"],
+        "write_bytes_per_launch": kq["wr"],
+        "traffic_bytes_per_launch": kq["rd"] + kq["wr"],
+        "algorithmic_read_bytes": kq["algo_rd"],
+        "algorithmic_write_bytes": kq["algo_wr"],
+        "other_kernels": {k: {kk: v for kk, v in r.items()} for k, r in rows.items() if k != "kq"},
     }
     json.dump(res, open(bench.TRAFFIC_FILE, "w"), indent=1)
-    md = ["# HBM traffic of kq_quantize (butterfly), 4608x3072 bf16", "",
-          "Commands (repository root, one MI355X):", "", "```",
-          "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch -o fetch -- python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --eager --calib-copy-mib %d" % mib,
-          "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write -o write -- python3 bench.py --steps 8 --warmup 2 --no-cpu --no-sq --eager --calib-copy-mib %d" % mib,
+    md = ["# HBM traffic of the quantizer kernels (FETCH_SIZE / WRITE_SIZE), one MI355X", "",
+          "Commands (repository root):", "", "```",
+          "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch -o fetch -- " + CMD % mib,
+          "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write -o write -- " + CMD % mib,
           "python3 bench_pmc.py gpurun_out/pmc %d" % mib, "```", "",
-          "| | counter (KiB/dispatch) | scale from the %d MiB copy | bytes per launch | algorithmic bytes |" % mib,
-          "|---|---|---|---|---|",
-          f"| read (FETCH_SIZE) | {res['fetch_size_kib_per_launch']:.1f} | {f_scale:.4f} | {rd:,.0f} | {algo_rd:,} |",
-          f"| write (WRITE_SIZE) | {res['write_size_kib_per_launch']:.1f} | {w_scale:.4f} | {wr:,.0f} | {algo_wr:,} |",
-          "", f"Total {rd + wr:,.0f} B per launch against {algo_rd + algo_wr:,} algorithmic "
-              f"({(rd + wr) / (algo_rd + algo_wr):.3f}x).", ""]
+          "Counters are medians per dispatch, scaled by what the same counter reads for a plain "
+          "%d MiB device copy (read scale %.4f, write scale %.4f)." % (mib, f_scale, w_scale), "",
+          "| kernel | read bytes / launch | algorithmic read | write bytes / launch | algorithmic write | total / algorithmic |",
+          "|---|---|---|---|---|---|"]
+    for key, r in rows.items():
+        md.append(f"| {r['what']} | {r['rd']:,.0f} | {r['algo_rd']:,} | {r['wr']:,.0f} | {r['algo_wr']:,} | "
+                  f"{(r['rd'] + r['wr']) / (r['algo_rd'] + r['algo_wr']):.3f}x |")
+    md += ["", f"kq_quantize: {kq['rd'] + kq['wr']:,.0f} B per launch against "
+               f"{kq['algo_rd'] + kq['algo_wr']:,} algorithmic; this figure is bench.py's roofline traffic "
+               "while the kernel sources hash to the value stored in the JSON beside this file.", ""]
     open(os.path.join(ROOT, "profiles", "kq_butterfly_flux_4608x3072_traffic.md"), "w").write("\n".join(md))
     print("\n".join(md))
 

@@ -40,6 +40,7 @@ def parse():
                     help="skip the SmoothQuant and block-Hadamard comparison timings")
     ap.add_argument("--no-weights", action="store_true", help="skip the weight-side timing")
     ap.add_argument("--no-gemm", action="store_true", help="skip the W4A4 product timing")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the 4608x12288 quantizer timing")
     ap.add_argument("--no-norm", action="store_true",
                     help="skip the normalization-fused quantizer timing")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -204,6 +205,36 @@ def norm_timing(args, cfg, xs, ps, qs, ss, kq_ms):
             "fused_over_quantizer_alone": round(f_ms / kq_ms, 4)}
 
 
+def mlp_timing(args):
+    """The same quantizer on the FLUX MLP input width, X[4608, 12288] bf16 (384 factor
+    sets), over 4 rotating sets (570 MB, beyond the last-level cache)."""
+    import torch
+
+    import synth
+    import online_activation_quantizer_amd as kq
+    cfg = synth.get_config("flux_mlp")
+    sets = 4
+    xs = [synth.make_activations_device(cfg, cfg.seed + 1000 * i).view(torch.int16) for i in range(sets)]
+    ps = [torch.from_numpy(synth.make_params(cfg.nb, np.random.default_rng(cfg.seed + i))).cuda()
+          for i in range(sets)]
+    qs = [torch.empty((cfg.rows, cfg.d // 2), dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    ss = [torch.empty((cfg.rows, cfg.d // 32), dtype=torch.uint8, device="cuda") for _ in range(sets)]
+
+    def step(i):
+        j = i % sets
+        kq.kq_quantize(xs[j], ps[j], q=qs[j], s=ss[j])
+
+    steps = max(8, args.steps // 4)
+    ms = (timed(step, steps, args.warmup, torch.cuda.current_stream()) if args.eager
+          else timed_graph(step, steps, args.warmup))
+    elems = cfg.rows * cfg.d
+    gbs = elems * BYTES_PER_ELEM / (ms * 1e-3) / 1e9
+    del xs, qs, ss
+    return {"workload": f"{cfg.rows}x{cfg.d} bf16, {cfg.nb} factor sets", "ms_per_call": round(ms, 6),
+            "gelem_s": round(elems / (ms * 1e-3) / 1e9, 3), "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 PEAK_FP4_TFLOPS = 10100.0  # dense fp4 matrix-core peak of one MI355X
 
 
@@ -332,6 +363,7 @@ def main():
     weights = None if args.no_weights else weights_timing(args)
     norm = None if args.no_norm else norm_timing(args, cfg, xs, ps, qs, ss, ms)
     gemm = None if args.no_gemm else gemm_timing(args, qs, ss)
+    mlp = None if args.no_mlp else mlp_timing(args)
     ceiling = None if args.no_ceiling else stream_ceiling(args, xs, qs, ss, ms)
 
     # parity of one production step against the oracle
@@ -388,6 +420,8 @@ def main():
         out["norm_fused"] = norm
     if gemm is not None:
         out["w4a4_gemm"] = gemm
+    if mlp is not None:
+        out["mlp_shape"] = mlp
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -16,12 +16,12 @@
 // plus that block's scale byte (chosen from a 32-bit register by op_sel).
 //
 // Tiling.  A workgroup (4 waves, 2 x 2) computes a 128 x 128 tile of Y; each wave a
-// 64 x 64 quarter as 2 x 2 MFMA tiles.  K advances 128 at a time: the 128 x 64-byte
-// code tiles of A and B and their 128 x 4 scale bytes are staged through LDS
-// (double-buffered, code rows padded to 80 bytes against bank conflicts), with the
-// global loads of the step after next in flight during this step's MFMAs.  Rows past M or N are
-// clamped on load and not stored; K-blocks past K load as code 0 with scale 2^0
-// (value 0).
+// 64 x 64 quarter as 2 x 2 MFMA tiles.  K advances 64 KSUB values at a time (256 by
+// default: 128 code bytes per row, whole cache lines): the code tiles of A and B
+// and their scale bytes are staged through LDS (double-buffered, code rows padded
+// by 16 bytes against bank conflicts), with the global loads of the step after
+// next in flight during this step's MFMAs.  Rows past M or N are clamped on load
+// and not stored; K-blocks past K load as code 0 with scale 2^0 (value 0).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,14 +34,23 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128, kBN = 128;
-constexpr int kBKBytes = 64;               // K = 128 fp4 values per step
-constexpr int kPitch = kBKBytes + 16;      // LDS code-row pitch
-constexpr int kTileCodes = 128 * kPitch;   // bytes per operand per stage
 constexpr uint32_t kScaleOne = 0x7F7F7F7Fu;  // four E8M0 bytes of 2^0
 
+#ifndef KQ_GEMM_KSUB
+#define KQ_GEMM_KSUB 4
+#endif
+// 64-element K substeps (one MFMA each) per staged K step: K step = 64 KSUB values,
+// 32 KSUB code bytes per row
+constexpr int kKSub = KQ_GEMM_KSUB;
+constexpr int kBKBytes = 32 * kKSub;
+constexpr int kPitch = kBKBytes + 16;      // LDS code-row pitch (bank spread)
+constexpr int kTileCodes = 128 * kPitch;   // bytes per operand per stage
+constexpr int kChunks = kKSub;             // 16-byte code chunks per thread per operand
+constexpr int kScaleWords = kKSub / 2;     // 32-bit scale words per row per step
+
 struct Stage {
-  uint4 a[2], b[2];  // this thread's two 16-byte code chunks of A and of B
-  uint32_t sc;       // one row's 4 scale bytes (threads 0-127: A, 128-255: B)
+  uint4 a[kChunks], b[kChunks];  // this thread's code chunks of A and of B
+  uint32_t sc[kScaleWords];      // one row's scale bytes (threads 0-127: A, 128-255: B)
 };
 
 template <bool OUT_BF16, bool SCALE_WORDS>
@@ -51,7 +60,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
     uint32_t M, uint32_t N, uint32_t K, void* __restrict__ out, uint32_t ldo, uint32_t tiles_n,
     uint32_t xcd_cols) {
   __shared__ __attribute__((aligned(16))) uint8_t codes[2][2][kTileCodes];  // [stage][A/B]
-  __shared__ uint32_t scales[2][2][128];
+  __shared__ uint32_t scales[2][2][128][kScaleWords];
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t wm = wave >> 1, wn = wave & 1u;
   // Tile order.  Workgroups go to the 8 XCDs round-robin by index; when xcd_cols > 0
@@ -69,15 +78,16 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
   }
   const uint32_t m0 = tm * kBM, n0 = tn * kBN;
   const uint32_t kbytes = K / 2, kblocks = K / 32;
-  const uint32_t nsteps = (K + 127) / 128;
+  const uint32_t nsteps = (K + 64 * kKSub - 1) / (64 * kKSub);
 
   // global -> register loads of one K step
   auto load_stage = [&](uint32_t step, Stage& st) {
     const uint32_t kb0 = step * kBKBytes;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t c = tid + 256u * i;       // chunk: row c / 4, 16-byte column c % 4
-      const uint32_t row = c >> 2, col = (c & 3u) * 16u;
+    for (int i = 0; i < kChunks; ++i) {
+      // chunk c: row c / (2 KSUB), 16-byte column c % (2 KSUB)
+      const uint32_t c = tid + 256u * i;
+      const uint32_t row = c / (2 * kKSub), col = (c % (2 * kKSub)) * 16u;
       const bool kin = kb0 + col < kbytes;
       const uint32_t ra = m0 + row < M ? m0 + row : M - 1;
       const uint32_t rb = n0 + row < N ? n0 + row : N - 1;
@@ -92,26 +102,33 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
     const bool isb = tid >= 128u;
     const uint32_t row = tid & 127u;
     const uint32_t r = isb ? (n0 + row < N ? n0 + row : N - 1) : (m0 + row < M ? m0 + row : M - 1);
-    const uint8_t* srow = (isb ? sb + (uint64_t)r * ldsb : sa + (uint64_t)r * ldsa) + step * 4u;
-    uint32_t w = kScaleOne;
-    if (SCALE_WORDS && step * 4u + 4u <= kblocks) {
-      w = *reinterpret_cast<const uint32_t*>(srow);
-    } else {
+    const uint32_t blk0 = step * 2u * kKSub;  // first scale byte of this step
+    const uint8_t* srow = (isb ? sb + (uint64_t)r * ldsb : sa + (uint64_t)r * ldsa) + blk0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (step * 4u + j < kblocks) w = (w & ~(0xFFu << (8 * j))) | ((uint32_t)srow[j] << (8 * j));
+    for (int wdx = 0; wdx < kScaleWords; ++wdx) {
+      uint32_t w = kScaleOne;
+      const uint32_t b0 = blk0 + 4u * wdx;
+      if (SCALE_WORDS && b0 + 4u <= kblocks) {
+        w = *reinterpret_cast<const uint32_t*>(srow + 4 * wdx);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (b0 + j < kblocks)
+            w = (w & ~(0xFFu << (8 * j))) | ((uint32_t)srow[4 * wdx + j] << (8 * j));
+      }
+      st.sc[wdx] = w;
     }
-    st.sc = w;
   };
   auto store_stage = [&](int buf, const Stage& st) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kChunks; ++i) {
       const uint32_t c = tid + 256u * i;
-      const uint32_t off = (c >> 2) * kPitch + (c & 3u) * 16u;
+      const uint32_t off = (c / (2 * kKSub)) * kPitch + (c % (2 * kKSub)) * 16u;
       *reinterpret_cast<uint4*>(&codes[buf][0][off]) = st.a[i];
       *reinterpret_cast<uint4*>(&codes[buf][1][off]) = st.b[i];
     }
-    scales[buf][tid >> 7][tid & 127u] = st.sc;
+#pragma unroll
+    for (int wdx = 0; wdx < kScaleWords; ++wdx) scales[buf][tid >> 7][tid & 127u][wdx] = st.sc[wdx];
   };
 
   v16f acc[2][2];
@@ -132,7 +149,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
   for (uint32_t step = 0; step < nsteps; ++step) {
     if (step + 2 < nsteps) load_stage(step + 2, far);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < kKSub; ++ks) {
       v8i A[2], B[2];
       uint32_t sA[2], sB[2];
 #pragma unroll
@@ -142,15 +159,16 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
         const uint4 vb = *reinterpret_cast<const uint4*>(&codes[buf][1][rb * kPitch + 32u * ks + 16u * h]);
         A[i] = v8i{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
         B[i] = v8i{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
-        // the lane's block scale moved to byte 2 ks (op_sel picks it)
-        sA[i] = scales[buf][0][ra] >> (8u * h);
-        sB[i] = scales[buf][1][rb] >> (8u * h);
+        // the lane's block scale (byte 2 ks + h of the row's step) moved to byte
+        // 2 (ks % 2) of its word, which op_sel picks
+        sA[i] = scales[buf][0][ra][ks / 2] >> (8u * h);
+        sB[i] = scales[buf][1][rb][ks / 2] >> (8u * h);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          if (ks == 0)
+          if (ks % 2 == 0)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 A[i], B[j], acc[i][j], 4, 4, 0, (int)sA[i], 0, (int)sB[j]);
           else

@@ -21,7 +21,8 @@
 // and their scale bytes are staged through LDS (double-buffered, code rows padded
 // by 16 bytes against bank conflicts), with the global loads of the step after
 // next in flight during this step's MFMAs.  Rows past M or N are clamped on load
-// and not stored; K-blocks past K load as code 0 with scale 2^0 (value 0).
+// and not stored; K-blocks past K get scale 2^-127 on both operands (their
+// products vanish).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,10 +32,10 @@ namespace kq {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // register-friendly 16 bytes
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128, kBN = 128;
-constexpr uint32_t kScaleOne = 0x7F7F7F7Fu;  // four E8M0 bytes of 2^0
 
 #ifndef KQ_GEMM_KSUB
 #define KQ_GEMM_KSUB 4
@@ -49,7 +50,7 @@ constexpr int kChunks = kKSub;             // 16-byte code chunks per thread per
 constexpr int kScaleWords = kKSub / 2;     // 32-bit scale words per row per step
 
 struct Stage {
-  uint4 a[kChunks], b[kChunks];  // this thread's code chunks of A and of B
+  u32x4 a[kChunks], b[kChunks];  // this thread's code chunks of A and of B
   uint32_t sc[kScaleWords];      // one row's scale bytes (threads 0-127: A, 128-255: B)
 };
 
@@ -80,7 +81,11 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
   const uint32_t kbytes = K / 2, kblocks = K / 32;
   const uint32_t nsteps = (K + 64 * kKSub - 1) / (64 * kKSub);
 
-  // global -> register loads of one K step
+  // global -> register loads of one K step.  No load sits under a branch (the
+  // compiler would then wait for every load in flight): code chunks past K re-read
+  // the row's last chunk, and their scale bytes on both operands are 0x00 (2^-127),
+  // so each of their products is below 36 * 2^-254 and vanishes in the fp32
+  // accumulation whatever the codes (E2M1 codes are all finite).
   auto load_stage = [&](uint32_t step, Stage& st) {
     const uint32_t kb0 = step * kBKBytes;
 #pragma unroll
@@ -88,35 +93,40 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
       // chunk c: row c / (2 KSUB), 16-byte column c % (2 KSUB)
       const uint32_t c = tid + 256u * i;
       const uint32_t row = c / (2 * kKSub), col = (c % (2 * kKSub)) * 16u;
-      const bool kin = kb0 + col < kbytes;
+      const uint32_t off = kb0 + col < kbytes ? kb0 + col : kbytes - 16u;
       const uint32_t ra = m0 + row < M ? m0 + row : M - 1;
       const uint32_t rb = n0 + row < N ? n0 + row : N - 1;
-      const uint4 za = kin ? *reinterpret_cast<const uint4*>(qa + (uint64_t)ra * lda + kb0 + col)
-                           : make_uint4(0, 0, 0, 0);
-      const uint4 zb = kin ? *reinterpret_cast<const uint4*>(qb + (uint64_t)rb * ldb + kb0 + col)
-                           : make_uint4(0, 0, 0, 0);
-      st.a[i] = za;
-      st.b[i] = zb;
+      st.a[i] = *reinterpret_cast<const u32x4*>(qa + (uint64_t)ra * lda + off);
+      st.b[i] = *reinterpret_cast<const u32x4*>(qb + (uint64_t)rb * ldb + off);
     }
     // scales: thread t < 128 takes A row t, t >= 128 takes B row t - 128
     const bool isb = tid >= 128u;
     const uint32_t row = tid & 127u;
     const uint32_t r = isb ? (n0 + row < N ? n0 + row : N - 1) : (m0 + row < M ? m0 + row : M - 1);
     const uint32_t blk0 = step * 2u * kKSub;  // first scale byte of this step
-    const uint8_t* srow = (isb ? sb + (uint64_t)r * ldsb : sa + (uint64_t)r * ldsa) + blk0;
+    const uint8_t* srow = isb ? sb + (uint64_t)r * ldsb : sa + (uint64_t)r * ldsa;
 #pragma unroll
     for (int wdx = 0; wdx < kScaleWords; ++wdx) {
-      uint32_t w = kScaleOne;
       const uint32_t b0 = blk0 + 4u * wdx;
-      if (SCALE_WORDS && b0 + 4u <= kblocks) {
-        w = *reinterpret_cast<const uint32_t*>(srow + 4 * wdx);
+      const uint32_t valid = b0 < kblocks ? kblocks - b0 : 0u;  // bytes of this word inside K
+      const uint32_t keep = valid >= 4u ? 0xFFFFFFFFu : (1u << (8u * valid)) - 1u;
+      uint32_t w;
+      if (SCALE_WORDS) {
+        // kblocks >= 4 here: read the last whole word when this one runs past the end
+        const uint32_t at = b0 + 4u <= kblocks ? b0 : kblocks - 4u;
+        const uint32_t raw = *reinterpret_cast<const uint32_t*>(srow + at);
+        const uint32_t sh = 8u * (b0 - at);  // 0 .. 24, or >= 32 wholly past the end
+        w = sh < 32u ? raw >> sh : 0u;
       } else {
+        // byte by byte from clamped addresses (no load under a branch)
+        w = 0u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (b0 + j < kblocks)
-            w = (w & ~(0xFFu << (8 * j))) | ((uint32_t)srow[4 * wdx + j] << (8 * j));
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t at = b0 + j < kblocks ? b0 + j : kblocks - 1u;
+          w |= (uint32_t)srow[at] << (8 * j);
+        }
       }
-      st.sc[wdx] = w;
+      st.sc[wdx] = w & keep;  // bytes past K: 0x00
     }
   };
   auto store_stage = [&](int buf, const Stage& st) {
@@ -124,8 +134,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
     for (int i = 0; i < kChunks; ++i) {
       const uint32_t c = tid + 256u * i;
       const uint32_t off = (c / (2 * kKSub)) * kPitch + (c % (2 * kKSub)) * 16u;
-      *reinterpret_cast<uint4*>(&codes[buf][0][off]) = st.a[i];
-      *reinterpret_cast<uint4*>(&codes[buf][1][off]) = st.b[i];
+      *reinterpret_cast<u32x4*>(&codes[buf][0][off]) = st.a[i];
+      *reinterpret_cast<u32x4*>(&codes[buf][1][off]) = st.b[i];
     }
 #pragma unroll
     for (int wdx = 0; wdx < kScaleWords; ++wdx) scales[buf][tid >> 7][tid & 127u][wdx] = st.sc[wdx];
@@ -155,8 +165,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const uint32_t ra = wm * 64u + 32u * i + lr, rb = wn * 64u + 32u * i + lr;
-        const uint4 va = *reinterpret_cast<const uint4*>(&codes[buf][0][ra * kPitch + 32u * ks + 16u * h]);
-        const uint4 vb = *reinterpret_cast<const uint4*>(&codes[buf][1][rb * kPitch + 32u * ks + 16u * h]);
+        const u32x4 va = *reinterpret_cast<const u32x4*>(&codes[buf][0][ra * kPitch + 32u * ks + 16u * h]);
+        const u32x4 vb = *reinterpret_cast<const u32x4*>(&codes[buf][1][rb * kPitch + 32u * ks + 16u * h]);
         A[i] = v8i{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
         B[i] = v8i{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
         // the lane's block scale (byte 2 ks + h of the row's step) moved to byte
@@ -176,10 +186,20 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
                 A[i], B[j], acc[i][j], 4, 4, 2, (int)sA[i], 2, (int)sB[j]);
         }
     }
+    // keep the next step's LDS stores (and their wait for its loads) after this
+    // step's products
+    __builtin_amdgcn_sched_barrier(0);
     if (step + 1 < nsteps) {
       // the other slot was last read before the previous barrier
       store_stage(buf ^ 1, nxt);
-      nxt = far;
+      // field by field (a struct copy here ends up in scratch memory)
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) {
+        nxt.a[i] = far.a[i];
+        nxt.b[i] = far.b[i];
+      }
+#pragma unroll
+      for (int wdx = 0; wdx < kScaleWords; ++wdx) nxt.sc[wdx] = far.sc[wdx];
       __syncthreads();
       buf ^= 1;
     }
@@ -223,9 +243,9 @@ hipError_t launch_mx_gemm(const GemmArgs& g) {
   const int64_t tiles_m = (g.M + kBM - 1) / kBM, tiles_n = (g.N + kBN - 1) / kBN;
   const int64_t grid = tiles_m * tiles_n;
   const int64_t xcd_cols = tiles_n % 8 == 0 ? tiles_n / 8 : 0;
-  // whole 32-bit scale words when every scale row starts 4-byte aligned
+  // whole 32-bit scale words when every scale row starts 4-byte aligned and holds one
   const bool words = ((uintptr_t)g.sa % 4 == 0) && ((uintptr_t)g.sb % 4 == 0) && g.ldsa % 4 == 0 &&
-                     g.ldsb % 4 == 0;
+                     g.ldsb % 4 == 0 && g.K >= 128;
   if (g.out_bf16) {
     if (words) launch_t<true, true>(g, grid, tiles_n, xcd_cols);
     else launch_t<true, false>(g, grid, tiles_n, xcd_cols);

@@ -44,10 +44,10 @@ struct Moments {
 
 // Merge of two sets (Chan, Golub and LeVeque's pairwise update).
 __device__ __forceinline__ Moments merge(const Moments& a, const Moments& b) {
+  // branch-free: two empty sets give wb = 0 and stay empty
   const float n = a.n + b.n;
-  if (n == 0.0f) return a;
   const float delta = b.mean - a.mean;
-  const float wb = b.n * __builtin_amdgcn_rcpf(n);  // exact for the power-of-two counts
+  const float wb = n > 0.0f ? b.n * __builtin_amdgcn_rcpf(n) : 0.0f;  // exact for power-of-two counts
   return {n, __builtin_fmaf(delta, wb, a.mean), a.m2 + b.m2 + delta * delta * (a.n * wb)};
 }
 
@@ -76,8 +76,12 @@ __device__ __forceinline__ Moments half_merge(Moments m) {
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) {
     const Moments o = {__shfl_xor(m.n, off), __shfl_xor(m.mean, off), __shfl_xor(m.m2, off)};
-    // both lanes of a pair merge in the same order so they end with equal values
-    m = (threadIdx.x & off) ? merge(o, m) : merge(m, o);
+    // both lanes of a pair merge in the same order (lower lane's set first) so they
+    // end with equal values; operands chosen by selects, not branches
+    const bool upper = (threadIdx.x & off) != 0;
+    const Moments lo = {upper ? o.n : m.n, upper ? o.mean : m.mean, upper ? o.m2 : m.m2};
+    const Moments hi = {upper ? m.n : o.n, upper ? m.mean : o.mean, upper ? m.m2 : o.m2};
+    m = merge(lo, hi);
   }
   return m;
 }

@@ -221,9 +221,10 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(
           // round to nearest even (finite values)
           const uint32_t u = __float_as_uint(v);
           const uint16_t hb = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-          reinterpret_cast<uint16_t*>(out)[(uint64_t)row * ldo + col] = hb;
+          // streaming stores: Y is not re-read here and must not evict the operand tiles
+          __builtin_nontemporal_store(hb, reinterpret_cast<uint16_t*>(out) + (uint64_t)row * ldo + col);
         } else {
-          reinterpret_cast<float*>(out)[(uint64_t)row * ldo + col] = acc[i][j][r];
+          __builtin_nontemporal_store(acc[i][j][r], reinterpret_cast<float*>(out) + (uint64_t)row * ldo + col);
         }
       }
     }

@@ -301,6 +301,38 @@ def weights_timing(args):
             "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def cpu_oracles(x0, p0, threads):
+    """The oracle of every other row timed on bounded samples of the same workloads
+    (host cores; about a second each), reported beside the GPU figures."""
+    import oracle
+    import synth
+
+    def rate(fn, elems):
+        t0 = time.perf_counter()
+        fn()
+        return elems / (time.perf_counter() - t0)
+
+    rows = 256
+    xs = np.ascontiguousarray(x0[:rows])
+    d = x0.shape[1]
+    out = {"threads": threads}
+    out["kq_quantize_1_thread_gelem_s"] = round(
+        rate(lambda: oracle.quantize(np.ascontiguousarray(x0[:64]), p0, nthreads=1), 64 * d) / 1e9, 5)
+    out["hq_quantize_gelem_s"] = round(rate(lambda: oracle.hadamard_quantize(xs, nthreads=threads), rows * d) / 1e9, 5)
+    shift, scale = synth.make_modulation(1, d, np.random.default_rng(7))
+    out["kq_norm_quantize_gelem_s"] = round(rate(
+        lambda: oracle.norm_quantize(xs, p0, shift, scale, rows, 1e-6, nthreads=threads), rows * d) / 1e9, 5)
+    w, pw = synth.make_weights(synth.get_weight_config("flux_w_mlp"))
+    ws = np.ascontiguousarray(w[:rows])
+    out["kq_quantize_weights_gelem_s"] = round(
+        rate(lambda: oracle.quantize_weights(ws, pw, nthreads=threads), rows * d) / 1e9, 5)
+    qa, sa, _ = oracle.quantize(xs, p0, nthreads=threads)
+    qb, sb, _ = oracle.quantize_weights(ws, pw, nthreads=threads)
+    out["w4a4_gemm_tflops"] = round(rate(lambda: oracle.mx_gemm(qa, sa, qb, sb), 2.0 * rows * rows * d) / 1e12, 6)
+    out["sample"] = f"{rows} rows of each workload (the product: {rows} x {rows} x {d})"
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -431,6 +463,10 @@ def main():
         del src, dst
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x0, p0, args.cpu_seconds)
+        try:
+            out["cpu_oracles"] = cpu_oracles(x0, p0, out["cpu_baseline"]["cores"])
+        except Exception as e:  # the oracle is test infrastructure; its absence does not stop timing
+            out["cpu_oracles"] = {"error": str(e)}
     print(json.dumps(out), flush=True)
 
 

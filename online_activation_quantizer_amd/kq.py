@@ -258,6 +258,9 @@ def kq_mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
     (codes [rows, K/2], scales [rows, K/32]); out float32 (default) or bfloat16."""
     import torch
     M, N, K = qa.shape[0], qb.shape[0], qa.shape[1] * 2
+    if qb.shape[1] != qa.shape[1] or tuple(sa.shape) != (M, K // 32) or tuple(sb.shape) != (N, K // 32):
+        raise KQError(KQ_ERR_SHAPE, "kq_mx_gemm: codes [rows, K/2] and scales [rows, K/32] of both operands "
+                                    "must agree on K")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=qa.device)
     code = {torch.float32: KQ_FP32, torch.bfloat16: KQ_BF16}.get(out.dtype)

@@ -194,3 +194,14 @@ def test_binding_rejects_unknown_dtype():
     import online_activation_quantizer_amd as kq
     with pytest.raises(kq.KQError):
         kq.kq_quantize(torch.zeros((2, 32), dtype=torch.float64), torch.zeros(15))
+
+
+def test_mx_gemm_binding_checks_operand_shapes():
+    torch = pytest.importorskip("torch")
+    import online_activation_quantizer_amd as kq
+    qa, sa = torch.zeros((4, 64), dtype=torch.uint8), torch.zeros((4, 4), dtype=torch.uint8)
+    qb, sb = torch.zeros((3, 48), dtype=torch.uint8), torch.zeros((3, 3), dtype=torch.uint8)
+    with pytest.raises(kq.KQError):
+        kq.kq_mx_gemm(qa, sa, qb, sb)       # K differs between the operands
+    with pytest.raises(kq.KQError):
+        kq.kq_mx_gemm(qa, sa[:, :3], qa, sa)  # scales do not cover K

@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-weights", action="store_true", help="skip the weight-side timing")
     ap.add_argument("--no-gemm", action="store_true", help="skip the W4A4 product timing")
     ap.add_argument("--no-mlp", action="store_true", help="skip the 4608x12288 quantizer timing")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the 28-call batched sweep (14 x 18432x3072 + 14 x 18432x12288)")
     ap.add_argument("--no-norm", action="store_true",
                     help="skip the normalization-fused quantizer timing")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -219,10 +221,15 @@ def mlp_timing(args):
           for i in range(sets)]
     qs = [torch.empty((cfg.rows, cfg.d // 2), dtype=torch.uint8, device="cuda") for _ in range(sets)]
     ss = [torch.empty((cfg.rows, cfg.d // 32), dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    if args.variant == "mfma":
+        ts = [kq.kq_expand_factors(p, kq.KQ_T_DENSE_BF16X3) for p in ps]
+        tfmt, var = kq.KQ_T_DENSE_BF16X3, kq.KQ_MFMA
+    else:
+        ts, tfmt, var = ps, kq.KQ_T_PARAMS, kq.KQ_BUTTERFLY
 
     def step(i):
         j = i % sets
-        kq.kq_quantize(xs[j], ps[j], q=qs[j], s=ss[j])
+        kq.kq_quantize(xs[j], ts[j], tfmt, var, q=qs[j], s=ss[j])
 
     steps = max(8, args.steps // 4)
     ms = (timed(step, steps, args.warmup, torch.cuda.current_stream()) if args.eager
@@ -230,9 +237,43 @@ def mlp_timing(args):
     elems = cfg.rows * cfg.d
     gbs = elems * BYTES_PER_ELEM / (ms * 1e-3) / 1e9
     del xs, qs, ss
-    return {"workload": f"{cfg.rows}x{cfg.d} bf16, {cfg.nb} factor sets", "ms_per_call": round(ms, 6),
+    return {"workload": f"{cfg.rows}x{cfg.d} bf16, {cfg.nb} factor sets, {args.variant}", "ms_per_call": round(ms, 6),
             "gelem_s": round(elems / (ms * 1e-3) / 1e9, 3), "gbs": round(gbs, 1),
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def sweep_timing(args):
+    """The batched sweep: 28 layer-shaped calls alternating X[18432, 3072] and
+    X[18432, 12288] bf16, each with its own inputs, factor set and outputs (10 GB moved,
+    no reuse between calls), replayed as one graph a few times; time per sweep."""
+    import torch
+
+    import synth
+    from synth.configs import SWEEP_CALLS, sweep_call
+    import online_activation_quantizer_amd as kq
+    calls = []
+    elems = 0
+    for i in range(SWEEP_CALLS):
+        cfg = sweep_call(i)
+        x = synth.make_activations_device(cfg, cfg.seed).view(torch.int16)
+        p = torch.from_numpy(synth.make_params(cfg.nb, np.random.default_rng(cfg.seed))).cuda()
+        q = torch.empty((cfg.rows, cfg.d // 2), dtype=torch.uint8, device="cuda")
+        s = torch.empty((cfg.rows, cfg.d // 32), dtype=torch.uint8, device="cuda")
+        calls.append((x, p, q, s))
+        elems += cfg.rows * cfg.d
+
+    def step(i):
+        for x, p, q, s in calls:
+            kq.kq_quantize(x, p, q=q, s=s)
+
+    reps = 3
+    ms = (timed(step, reps, 1, torch.cuda.current_stream()) if args.eager else timed_graph(step, reps, 1))
+    gbs = elems * BYTES_PER_ELEM / (ms * 1e-3) / 1e9
+    del calls
+    torch.cuda.empty_cache()
+    return {"workload": "14 x 18432x3072 + 14 x 18432x12288 bf16, own inputs and factors per call",
+            "ms_per_sweep": round(ms, 4), "gelem_s": round(elems / (ms * 1e-3) / 1e9, 3),
+            "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 PEAK_FP4_TFLOPS = 10100.0  # dense fp4 matrix-core peak of one MI355X
@@ -396,6 +437,7 @@ def main():
     norm = None if args.no_norm else norm_timing(args, cfg, xs, ps, qs, ss, ms)
     gemm = None if args.no_gemm else gemm_timing(args, qs, ss)
     mlp = None if args.no_mlp else mlp_timing(args)
+    sweep = None if args.no_sweep else sweep_timing(args)
     ceiling = None if args.no_ceiling else stream_ceiling(args, xs, qs, ss, ms)
 
     # parity of one production step against the oracle
@@ -454,6 +496,8 @@ def main():
         out["w4a4_gemm"] = gemm
     if mlp is not None:
         out["mlp_shape"] = mlp
+    if sweep is not None:
+        out["sweep_28_calls"] = sweep
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -102,9 +102,9 @@ def main():
     json.dump(res, open(bench.TRAFFIC_FILE, "w"), indent=1)
     md = ["# HBM traffic of the quantizer kernels (FETCH_SIZE / WRITE_SIZE), one MI355X", "",
           "Commands (repository root):", "", "```",
-          "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch -o fetch -- " + CMD % mib,
-          "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write -o write -- " + CMD % mib,
-          "python3 bench_pmc.py gpurun_out/pmc %d" % mib, "```", "",
+          "rocprofv3 --pmc FETCH_SIZE --output-format csv -d out/pmc/fetch -o fetch -- " + CMD % mib,
+          "rocprofv3 --pmc WRITE_SIZE --output-format csv -d out/pmc/write -o write -- " + CMD % mib,
+          "python3 bench_pmc.py out/pmc %d" % mib, "```", "",
           "Counters are medians per dispatch, scaled by what the same counter reads for a plain "
           "%d MiB device copy (read scale %.4f, write scale %.4f)." % (mib, f_scale, w_scale), "",
           "| kernel | read bytes / launch | algorithmic read | write bytes / launch | algorithmic write | total / algorithmic |",
@@ -160,9 +160,9 @@ def trace(trace_dir, bench_json):
 
     md = ["# Kernel trace of bench.py, FLUX.1-schnell-like 4608x3072 bf16 workload (one MI355X)", "",
           "Commands (repository root):", "", "```",
-          "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o bench -- python3 bench.py --no-cpu",
-          "python3 bench.py > gpurun_out/bench.json",
-          "python3 bench_pmc.py trace gpurun_out/trace gpurun_out/bench.json", "```", "",
+          "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o bench -- python3 bench.py --no-cpu",
+          "python3 bench.py > out/bench.json",
+          "python3 bench_pmc.py trace out/trace out/bench.json", "```", "",
           "bench.py replays each timed leg from one captured HIP graph (16 rotating buffer sets for the "
           "4608x3072 legs).  Durations from the trace (end - start per dispatch), microseconds:", "",
           "| kernel | dispatches | average | median | p10 | p90 |", "|---|---|---|---|---|---|"]

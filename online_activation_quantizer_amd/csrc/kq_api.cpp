@@ -297,8 +297,11 @@ int kq_mx_gemm(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
   if (!aligned(qa, 16) || !aligned(qb, 16) || lda % 16 != 0 || ldb % 16 != 0 ||
       !aligned(out, out_dtype == KQ_FP32 ? 4 : 2))
     return KQ_ERR_ALIGN;
+  int cus = 0;
+  const int rc = current_cus(&cus);
+  if (rc != KQ_OK) return rc;
   const kq::GemmArgs g{qa, lda, sa, ldsa, qb, ldb, sb, ldsb, M, N, K, out, ldo,
-                       out_dtype == KQ_BF16, stream};
+                       out_dtype == KQ_BF16, stream, cus};
   const hipError_t e = kq::launch_mx_gemm(g);
   return e == hipSuccess ? KQ_OK : fail_hip(e);
 }

@@ -13,16 +13,22 @@
 // K-values of each row (OCP MX block size) in hardware, accumulating in fp32.  Lane
 // l supplies row l % 32 and the 32 K-values 32 (l / 32) .. + 31 as 16 bytes, low
 // nibble first, which is exactly one 32-element block of the quantizer's layout,
-// plus that block's scale byte (chosen from a 32-bit register by op_sel).
+// plus that block's scale byte (chosen from a 32-bit register by op_sel).  The
+// weight tile goes in as the instruction's first operand and the activation tile as
+// its second, so the product comes out transposed: lane l holds row l % 32 of Y and
+// four consecutive columns per register quad, stored as one 8-byte (bf16) or
+// 16-byte (fp32) write.
 //
-// Tiling.  A workgroup (4 waves, 2 x 2) computes a 128 x 128 tile of Y; each wave a
-// 64 x 64 quarter as 2 x 2 MFMA tiles.  K advances 64 KSUB values at a time (256 by
-// default: 128 code bytes per row, whole cache lines): the code tiles of A and B
-// and their scale bytes are staged through LDS (double-buffered, code rows padded
-// by 16 bytes against bank conflicts), with the global loads of the step after
-// next in flight during this step's MFMAs.  Rows past M or N are clamped on load
-// and not stored; K-blocks past K get scale 2^-127 on both operands (their
-// products vanish).
+// Tiling.  A workgroup of 8 waves (2 x 4) computes 256 x 256 tiles of Y, each wave
+// a 128 x 64 part as 4 x 2 MFMA tiles (reading 0.75 KB of LDS per MFMA).  K
+// advances 256 values per step (128 code bytes per row, whole cache lines): the code
+// tiles of A and B and their scale bytes are staged through LDS (two slots, code rows
+// padded by 16 bytes against bank conflicts; 152 KB), from one register stage whose
+// global loads run a step ahead.  The grid is persistent (one workgroup per compute
+// unit, tiles strided by the grid), and the step sequence runs across tile
+// boundaries: the next tile's first steps load while a tile's last step multiplies
+// and its outputs are written.  Rows past M or N are clamped on load and not stored;
+// K-blocks past K get scale 2^-127 on both operands (their products vanish).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,9 +39,9 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // register-friendly 16 bytes
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-
-constexpr int kBM = 128, kBN = 128;
 
 #ifndef KQ_GEMM_KSUB
 #define KQ_GEMM_KSUB 4
@@ -44,215 +50,459 @@ constexpr int kBM = 128, kBN = 128;
 // 32 KSUB code bytes per row
 constexpr int kKSub = KQ_GEMM_KSUB;
 constexpr int kBKBytes = 32 * kKSub;
+constexpr int kRowChunks = kBKBytes / 16;  // 16-byte code chunks per row per step
 constexpr int kPitch = kBKBytes + 16;      // LDS code-row pitch (bank spread)
-constexpr int kTileCodes = 128 * kPitch;   // bytes per operand per stage
-constexpr int kChunks = kKSub;             // 16-byte code chunks per thread per operand
 constexpr int kScaleWords = kKSub / 2;     // 32-bit scale words per row per step
 
-struct Stage {
-  u32x4 a[kChunks], b[kChunks];  // this thread's code chunks of A and of B
-  uint32_t sc[kScaleWords];      // one row's scale bytes (threads 0-127: A, 128-255: B)
+// Workgroup tiling: WAVES_M x WAVES_N waves, each computing TM x TN tiles of 32 x 32.
+template <int WAVES_M, int WAVES_N, int TM, int TN>
+struct Tiling {
+  static constexpr int kWavesN = WAVES_N, kTM = TM, kTN = TN;
+  static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+  static constexpr int kBM = 32 * TM * WAVES_M, kBN = 32 * TN * WAVES_N;
+  static constexpr int kRows = kBM + kBN;  // LDS rows per slot: A's, then B's
+  static constexpr int kChunks = kRows * kRowChunks / kThreads;  // code chunks per thread
+  static constexpr int kChunksA = kBM * kRowChunks / kThreads;   // of which from A
+  static constexpr int kScaleRows = (kRows + kThreads - 1) / kThreads;
+  static_assert(kBM * kRowChunks % kThreads == 0 && kBN * kRowChunks % kThreads == 0,
+                "each thread's code chunks must split evenly between the operands");
+  static_assert(kThreads % kRowChunks == 0, "a thread keeps its chunk column across rows");
+  // staged output: each wave's 32 TM x 64 part goes through a 64-row region of one
+  // LDS slot (64 code-row pitches per wave)
+  static constexpr bool kCanStage = TN == 2 && TM % 2 == 0 && WAVES_M * WAVES_N * 64 * kPitch <= kRows * kPitch;
 };
 
-template <bool OUT_BF16, bool SCALE_WORDS>
-__global__ __launch_bounds__(256) void mx_gemm_kernel(
+#ifndef KQ_GEMM_CFG
+#define KQ_GEMM_CFG 1
+#endif
+#if KQ_GEMM_CFG == 0
+using Big = Tiling<2, 2, 2, 2>;  // 128 x 128, 4 waves of 64 x 64
+#elif KQ_GEMM_CFG == 1
+using Big = Tiling<2, 4, 4, 2>;  // 256 x 256, 8 waves of 128 x 64
+#elif KQ_GEMM_CFG == 3
+using Big = Tiling<2, 4, 2, 2>;  // 128 x 256, 8 waves of 64 x 64
+#elif KQ_GEMM_CFG == 4
+using Big = Tiling<4, 2, 2, 2>;  // 256 x 128, 8 waves of 64 x 64
+#elif KQ_GEMM_CFG == 5
+using Big = Tiling<1, 4, 4, 2>;  // 128 x 256, 4 waves of 128 x 64
+#endif
+#ifndef KQ_GEMM_WG_PER_CU
+#define KQ_GEMM_WG_PER_CU 1
+#endif
+
+// One K step of this thread's share of both operands, as loaded (scale words are
+// shifted and masked when stored to LDS, so no arithmetic waits on a load early).
+template <class T, bool SCALE_WORDS>
+struct Stage {
+  u32x4 c[T::kChunks];                                          // code chunks
+  uint32_t sc[T::kScaleRows][kScaleWords * (SCALE_WORDS ? 1 : 4)];  // scale words (or bytes)
+};
+
+// Output paths (EPI): kEpiScalar one output per store; kEpiVec4 four consecutive
+// outputs per store straight from the accumulators (N and ldo multiples of 4, output
+// 8- or 16-byte aligned); kEpiStaged (bf16 only; N and ldo multiples of 8, output
+// 16-byte aligned) the tile goes through LDS so that each store instruction writes
+// whole 128-byte row segments.
+constexpr int kEpiScalar = 0, kEpiVec4 = 1, kEpiStaged = 2;
+
+
+template <class T, bool OUT_BF16, int EPI, bool SCALE_WORDS>
+__global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void mx_gemm_kernel(
     const uint8_t* __restrict__ qa, uint32_t lda, const uint8_t* __restrict__ sa, uint32_t ldsa,
     const uint8_t* __restrict__ qb, uint32_t ldb, const uint8_t* __restrict__ sb, uint32_t ldsb,
     uint32_t M, uint32_t N, uint32_t K, void* __restrict__ out, uint32_t ldo, uint32_t tiles_n,
-    uint32_t xcd_cols) {
-  __shared__ __attribute__((aligned(16))) uint8_t codes[2][2][kTileCodes];  // [stage][A/B]
-  __shared__ uint32_t scales[2][2][128][kScaleWords];
+    uint32_t ntiles, uint32_t xcd_cols) {
+  constexpr int kRows = T::kRows, kBM = T::kBM, kThreads = T::kThreads;
+  static_assert(EPI != kEpiStaged || (OUT_BF16 && T::kCanStage), "staged output: bf16, tiles that fit");
+  __shared__ __attribute__((aligned(16))) uint8_t codes[2][kRows * kPitch];  // [slot], A rows then B rows
+  __shared__ __attribute__((aligned(8))) uint32_t scales[2][kRows][kScaleWords];
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-  const uint32_t wm = wave >> 1, wn = wave & 1u;
-  // Tile order.  Workgroups go to the 8 XCDs round-robin by index; when xcd_cols > 0
-  // (tiles_n = 8 xcd_cols) XCD x gets the tile columns [x xcd_cols, (x+1) xcd_cols)
-  // for every tile row, so the B tiles it reads stay in its own L2 while the tile
-  // rows advance, and consecutive workgroups on an XCD share their A tile.
-  uint32_t tm, tn;
-  if (xcd_cols) {
-    const uint32_t x = blockIdx.x & 7u, local = blockIdx.x >> 3;
-    tm = local / xcd_cols;
-    tn = x * xcd_cols + (local - tm * xcd_cols);
-  } else {
-    tm = blockIdx.x / tiles_n;
-    tn = blockIdx.x - tm * tiles_n;
-  }
-  const uint32_t m0 = tm * kBM, n0 = tn * kBN;
+  const uint32_t wm = wave / T::kWavesN, wn = wave % T::kWavesN;
+  const uint32_t grid = gridDim.x;
   const uint32_t kbytes = K / 2, kblocks = K / 32;
   const uint32_t nsteps = (K + 64 * kKSub - 1) / (64 * kKSub);
 
-  // global -> register loads of one K step.  No load sits under a branch (the
-  // compiler would then wait for every load in flight): code chunks past K re-read
-  // the row's last chunk, and their scale bytes on both operands are 0x00 (2^-127),
-  // so each of their products is below 36 * 2^-254 and vanishes in the fp32
-  // accumulation whatever the codes (E2M1 codes are all finite).
-  auto load_stage = [&](uint32_t step, Stage& st) {
-    const uint32_t kb0 = step * kBKBytes;
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      // chunk c: row c / (2 KSUB), 16-byte column c % (2 KSUB)
-      const uint32_t c = tid + 256u * i;
-      const uint32_t row = c / (2 * kKSub), col = (c % (2 * kKSub)) * 16u;
-      const uint32_t off = kb0 + col < kbytes ? kb0 + col : kbytes - 16u;
-      const uint32_t ra = m0 + row < M ? m0 + row : M - 1;
-      const uint32_t rb = n0 + row < N ? n0 + row : N - 1;
-      st.a[i] = *reinterpret_cast<const u32x4*>(qa + (uint64_t)ra * lda + off);
-      st.b[i] = *reinterpret_cast<const u32x4*>(qb + (uint64_t)rb * ldb + off);
+  // Tile t -> first row and column.  Workgroups go to the 8 XCDs round-robin by
+  // index and the grid is a multiple of 8, so all tiles of a workgroup share
+  // t % 8; when xcd_cols > 0 (tiles_n = 8 xcd_cols) XCD x gets the tile columns
+  // [x xcd_cols, (x+1) xcd_cols) for every tile row, so the B tiles it reads stay in
+  // its own L2 while the tile rows advance, and workgroups running together on an
+  // XCD share their A tiles.
+  auto tile_origin = [&](uint32_t t, uint32_t& m0, uint32_t& n0) {
+    uint32_t tm, tn;
+    if (xcd_cols) {
+      const uint32_t x = t & 7u, local = t >> 3;
+      tm = local / xcd_cols;
+      tn = x * xcd_cols + (local - tm * xcd_cols);
+    } else {
+      tm = t / tiles_n;
+      tn = t - tm * tiles_n;
     }
-    // scales: thread t < 128 takes A row t, t >= 128 takes B row t - 128
-    const bool isb = tid >= 128u;
-    const uint32_t row = tid & 127u;
-    const uint32_t r = isb ? (n0 + row < N ? n0 + row : N - 1) : (m0 + row < M ? m0 + row : M - 1);
-    const uint32_t blk0 = step * 2u * kKSub;  // first scale byte of this step
-    const uint8_t* srow = isb ? sb + (uint64_t)r * ldsb : sa + (uint64_t)r * ldsa;
-#pragma unroll
-    for (int wdx = 0; wdx < kScaleWords; ++wdx) {
-      const uint32_t b0 = blk0 + 4u * wdx;
-      const uint32_t valid = b0 < kblocks ? kblocks - b0 : 0u;  // bytes of this word inside K
-      const uint32_t keep = valid >= 4u ? 0xFFFFFFFFu : (1u << (8u * valid)) - 1u;
-      uint32_t w;
-      if (SCALE_WORDS) {
-        // kblocks >= 4 here: read the last whole word when this one runs past the end
-        const uint32_t at = b0 + 4u <= kblocks ? b0 : kblocks - 4u;
-        const uint32_t raw = *reinterpret_cast<const uint32_t*>(srow + at);
-        const uint32_t sh = 8u * (b0 - at);  // 0 .. 24, or >= 32 wholly past the end
-        w = sh < 32u ? raw >> sh : 0u;
-      } else {
-        // byte by byte from clamped addresses (no load under a branch)
-        w = 0u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t at = b0 + j < kblocks ? b0 + j : kblocks - 1u;
-          w |= (uint32_t)srow[at] << (8 * j);
-        }
-      }
-      st.sc[wdx] = w & keep;  // bytes past K: 0x00
-    }
-  };
-  auto store_stage = [&](int buf, const Stage& st) {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const uint32_t c = tid + 256u * i;
-      const uint32_t off = (c / (2 * kKSub)) * kPitch + (c % (2 * kKSub)) * 16u;
-      *reinterpret_cast<u32x4*>(&codes[buf][0][off]) = st.a[i];
-      *reinterpret_cast<u32x4*>(&codes[buf][1][off]) = st.b[i];
-    }
-#pragma unroll
-    for (int wdx = 0; wdx < kScaleWords; ++wdx) scales[buf][tid >> 7][tid & 127u][wdx] = st.sc[wdx];
+    m0 = tm * kBM;
+    n0 = tn * T::kBN;
   };
 
-  v16f acc[2][2];
+  // The rows this thread loads for the tile being fetched (origin lm0, ln0): code
+  // chunk i is LDS row (tid + kThreads i) / kRowChunks (the first kChunksA of them A
+  // rows), scale row j is LDS row tid + kThreads j (past the last row a duplicate
+  // whose value is not stored).  Rows past M or N re-read the matrix's last row and
+  // their products are not stored.
+  uint32_t lm0 = 0, ln0 = 0;
+  auto set_rows = [&](uint32_t t) { tile_origin(t, lm0, ln0); };
+  auto code_row = [&](int i) -> const uint8_t* {
+    const uint32_t r = (tid + kThreads * i) / kRowChunks;
+    if (i < T::kChunksA) {
+      const uint32_t g = lm0 + r < M ? lm0 + r : M - 1;
+      return qa + (uint64_t)g * lda;
+    }
+    const uint32_t g = ln0 + (r - kBM) < N ? ln0 + (r - kBM) : N - 1;
+    return qb + (uint64_t)g * ldb;
+  };
+  auto scale_row = [&](int j) -> const uint8_t* {
+    const uint32_t r0 = tid + kThreads * j, r = r0 < (uint32_t)kRows ? r0 : kRows - 1;
+    if (r < (uint32_t)kBM) {
+      const uint32_t g = lm0 + r < M ? lm0 + r : M - 1;
+      return sa + (uint64_t)g * ldsa;
+    }
+    const uint32_t g = ln0 + (r - kBM) < N ? ln0 + (r - kBM) : N - 1;
+    return sb + (uint64_t)g * ldsb;
+  };
+
+  // global -> register loads of K step `step` of the current rows.  No load sits
+  // under a branch (the compiler would then wait for every load in flight): code
+  // chunks past K re-read the row's last chunk, and their scale bytes on both
+  // operands become 0x00 (2^-127) when stored, so each of their products is below
+  // 36 * 2^-254 and vanishes in the fp32 accumulation whatever the codes (E2M1 codes
+  // are finite).
+  auto load_stage = [&](uint32_t step, Stage<T, SCALE_WORDS>& st) {
+    const uint32_t kb0 = step * kBKBytes;
+    const uint32_t col = 16u * (tid % kRowChunks);
+    // this thread's column in the row: past K, the row's last chunk
+    const uint32_t at = kb0 + col < kbytes ? kb0 + col : kbytes - 16u;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < T::kChunks; ++i) st.c[i] = *reinterpret_cast<const u32x4*>(code_row(i) + at);
+    const uint32_t blk0 = step * 2u * kKSub;  // first scale byte of this step
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < T::kScaleRows; ++j) {
+      const uint8_t* srow = scale_row(j);
+#pragma unroll
+      for (int wdx = 0; wdx < kScaleWords; ++wdx) {
+        const uint32_t b0 = blk0 + 4u * wdx;
+        if (SCALE_WORDS) {
+          // kblocks >= 4 here: read the last whole word when this one runs past the end
+          const uint32_t w_at = b0 + 4u <= kblocks ? b0 : kblocks - 4u;
+          st.sc[j][wdx] = *reinterpret_cast<const uint32_t*>(srow + w_at);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t b_at = b0 + q < kblocks ? b0 + q : kblocks - 1u;
+            st.sc[j][4 * wdx + q] = srow[b_at];
+          }
+        }
+      }
+    }
+  };
+  auto store_stage = [&](int slot, uint32_t step, const Stage<T, SCALE_WORDS>& st) {
+#pragma unroll
+    for (int i = 0; i < T::kChunks; ++i) {
+      const uint32_t c = tid + kThreads * i;
+      *reinterpret_cast<u32x4*>(&codes[slot][(c / kRowChunks) * kPitch + (c % kRowChunks) * 16u]) = st.c[i];
+    }
+    const uint32_t blk0 = step * 2u * kKSub;
+#pragma unroll
+    for (int j = 0; j < T::kScaleRows; ++j) {
+      const uint32_t r = tid + kThreads * j;
+#pragma unroll
+      for (int wdx = 0; wdx < kScaleWords; ++wdx) {
+        const uint32_t b0 = blk0 + 4u * wdx;
+        const uint32_t valid = b0 < kblocks ? kblocks - b0 : 0u;  // bytes of this word inside K
+        const uint32_t keep = valid >= 4u ? 0xFFFFFFFFu : (1u << (8u * valid)) - 1u;
+        uint32_t w;
+        if (SCALE_WORDS) {
+          const uint32_t at = b0 + 4u <= kblocks ? b0 : kblocks - 4u;
+          const uint32_t sh = 8u * (b0 - at);  // 0 .. 24, or >= 32 wholly past the end
+          w = sh < 32u ? st.sc[j][wdx] >> sh : 0u;
+        } else {
+          w = st.sc[j][4 * wdx] | (st.sc[j][4 * wdx + 1] << 8) | (st.sc[j][4 * wdx + 2] << 16) |
+              (st.sc[j][4 * wdx + 3] << 24);
+        }
+        if (kRows % kThreads == 0 || r < (uint32_t)kRows) scales[slot][r][wdx] = w & keep;  // past K: 0x00
+      }
+    }
+  };
+
+  // acc[i][j]: the wave's A row tile i (32 rows of Y) times its B row tile j (32
+  // columns of Y)
+  v16f acc[T::kTM][T::kTN];
+#pragma unroll
+  for (int i = 0; i < T::kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::kTN; ++j) acc[i][j] = v16f{};
 
   const uint32_t lr = lane & 31u, h = lane >> 5;
-  // step s is computed from LDS while step s + 1 waits in registers for its LDS
-  // slot and step s + 2 is in flight from memory
-  Stage nxt, far;
-  load_stage(0, nxt);
-  store_stage(0, nxt);
-  if (nsteps > 1) load_stage(1, nxt);
+  // this step's 8 scale bytes of each of the wave's A and B row tiles (lane row lr)
+  struct Scales {
+    uint32_t a[T::kTM][kScaleWords], b[T::kTN][kScaleWords];
+  };
+  auto read_scales = [&](int slot, Scales& sc) {
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i) {
+      const uint32_t r = wm * (32u * T::kTM) + 32u * i + lr;
+#pragma unroll
+      for (int w = 0; w < kScaleWords; ++w) sc.a[i][w] = scales[slot][r][w];
+    }
+#pragma unroll
+    for (int j = 0; j < T::kTN; ++j) {
+      const uint32_t r = kBM + wn * (32u * T::kTN) + 32u * j + lr;
+#pragma unroll
+      for (int w = 0; w < kScaleWords; ++w) sc.b[j][w] = scales[slot][r][w];
+    }
+  };
+  // the products of one 64-wide K substep
+  auto compute_ks = [&](int slot, int ks, const Scales& sc) {
+    v8i A[T::kTM], B[T::kTN];
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i) {
+      const uint32_t r = wm * (32u * T::kTM) + 32u * i + lr;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&codes[slot][r * kPitch + 32u * ks + 16u * h]);
+      A[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < T::kTN; ++j) {
+      const uint32_t r = kBM + wn * (32u * T::kTN) + 32u * j + lr;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&codes[slot][r * kPitch + 32u * ks + 16u * h]);
+      B[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::kTN; ++j) {
+        // the lane's block scale (byte 2 ks + h of the row's step) moved to byte
+        // 2 (ks % 2) of its word, which op_sel picks; B is the first operand
+        const int sA = (int)(sc.a[i][ks / 2] >> (8u * h)), sB = (int)(sc.b[j][ks / 2] >> (8u * h));
+        if (ks % 2 == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(B[j], A[i], acc[i][j], 4, 4, 0, sB, 0, sA);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(B[j], A[i], acc[i][j], 4, 4, 2, sB, 2, sA);
+      }
+  };
+
+  // acc[i][j][4 q + e]: Y row lr of the wave's A tile i, column 8 q + 4 h + e of its
+  // B tile j
+  auto write_tile = [&](uint32_t t) {
+    uint32_t m0, n0;
+    tile_origin(t, m0, n0);
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i) {
+      const uint32_t row = m0 + wm * (32u * T::kTM) + 32u * i + lr;
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < T::kTN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t col = n0 + wn * (32u * T::kTN) + 32u * j + 8u * q + 4u * h;
+          const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                              acc[i][j][4 * q + 3]};
+          if (OUT_BF16) {
+            uint32_t b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // round to nearest even (finite values)
+              const uint32_t u = __float_as_uint(v[e]);
+              b[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+            }
+            uint16_t* p = reinterpret_cast<uint16_t*>(out) + (uint64_t)row * ldo + col;
+            if (EPI == kEpiVec4) {
+              if (col < N) *reinterpret_cast<u32x2*>(p) = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < N) p[e] = (uint16_t)b[e];
+            }
+          } else {
+            float* p = reinterpret_cast<float*>(out) + (uint64_t)row * ldo + col;
+            if (EPI == kEpiVec4) {
+              if (col < N) *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < N) p[e] = v[e];
+            }
+          }
+        }
+    }
+  };
+
+  // The tile through LDS slot `slot` (free at this point): each wave turns its 128 x
+  // 64 part into bf16 rows in its own 64-row region of the slot (two halves), reads
+  // them back as 16-byte pieces and stores them, 8 lanes per 128-byte row segment, so
+  // every store instruction writes whole cache lines.  Only the wave's own lanes
+  // share its region; one workgroup barrier at the end frees the slot for the next
+  // step's operands.  The stores are buffer
+  // stores whose descriptor spans the tile's rows of Y; pieces past N get an offset
+  // outside it, so the hardware drops them with no branch.
+  auto write_tile_staged = [&](uint32_t t, int slot) {
+    uint32_t m0, n0;
+    tile_origin(t, m0, n0);
+    uint8_t* st = codes[slot] + wave * (64u * kPitch);
+    const uint32_t rows = M - m0 < (uint32_t)kBM ? M - m0 : (uint32_t)kBM;  // rows of Y in this tile
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<uint16_t*>(out) + (uint64_t)m0 * ldo, 0, (int)(rows * ldo * 2u), 0x00020000);
+#pragma unroll
+    for (int half = 0; half < T::kTM / 2; ++half) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < T::kTN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // round to nearest even (finite values)
+              const uint32_t u = __float_as_uint(acc[2 * half + ii][j][4 * q + e]);
+              b[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+            }
+            *reinterpret_cast<u32x2*>(st + (32u * ii + lr) * kPitch + (32u * j + 8u * q + 4u * h) * 2u) =
+                u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+          }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t r = lane / 8u + 8u * k, c = lane % 8u;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * kPitch + c * 16u);
+        const uint32_t row = wm * (32u * T::kTM) + 64u * half + r;  // in the tile
+        const uint32_t col = n0 + wn * 64u + 8u * c;
+        const uint32_t off = col < N ? (row * ldo + col) * 2u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)off, 0, 0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // the next step stores its operands into this slot
+    __syncthreads();
+  };
+
+  // The step sequence of this workgroup: its tiles blockIdx.x, + grid, ... (my_tiles
+  // of them), nsteps K steps each.  One register stage S: during step g (LDS slot
+  // g % 2), after the products of its first substep, S (step g + 1, loaded during
+  // step g - 1) goes to the other slot and the loads of step g + 2 start into S, so
+  // each load has a step of products to arrive.  Every load is issued
+  // unconditionally (past the last step of the last tile, the last tile's rows are
+  // re-read), so the only wait for memory is the one before S goes to LDS.
+  const uint32_t my_tiles = (ntiles - 1u - blockIdx.x) / grid + 1u;  // grid <= ntiles
+  const uint32_t total = my_tiles * nsteps;
+  uint32_t l_tile = blockIdx.x, l_step = 0;  // the step the next load fetches
+  set_rows(l_tile);
+  Stage<T, SCALE_WORDS> S;
+  uint32_t s_step = 0;  // K step held in S
+  auto load_next = [&]() {
+    s_step = l_step;
+    load_stage(l_step, S);
+    if (++l_step == nsteps) {
+      l_step = 0;
+      l_tile += grid;
+      if (l_tile < ntiles) set_rows(l_tile);
+    }
+  };
+  load_next();
+  store_stage(0, s_step, S);
+  load_next();
   __syncthreads();
-  int buf = 0;
-  for (uint32_t step = 0; step < nsteps; ++step) {
-    if (step + 2 < nsteps) load_stage(step + 2, far);
+  uint32_t c_tile = blockIdx.x, c_step = 0;
+  for (uint32_t g = 0; g < total; ++g) {
+    const int slot = (int)(g & 1u);
+    Scales sc;
+    read_scales(slot, sc);
+#ifndef KQ_GEMM_PINGPONG
+#define KQ_GEMM_PINGPONG 0
+#endif
+#if KQ_GEMM_PINGPONG
+    const bool early = wave >= (uint32_t)(kThreads / 128);  // second half of the waves
+    if (early) {
+      store_stage(slot ^ 1, s_step, S);
+      load_next();
+    }
+#pragma unroll
+    for (int ks = 0; ks < kKSub; ++ks) compute_ks(slot, ks, sc);
+    if (!early) {
+      store_stage(slot ^ 1, s_step, S);
+      load_next();
+    }
+#else
 #pragma unroll
     for (int ks = 0; ks < kKSub; ++ks) {
-      v8i A[2], B[2];
-      uint32_t sA[2], sB[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t ra = wm * 64u + 32u * i + lr, rb = wn * 64u + 32u * i + lr;
-        const u32x4 va = *reinterpret_cast<const u32x4*>(&codes[buf][0][ra * kPitch + 32u * ks + 16u * h]);
-        const u32x4 vb = *reinterpret_cast<const u32x4*>(&codes[buf][1][rb * kPitch + 32u * ks + 16u * h]);
-        A[i] = v8i{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
-        B[i] = v8i{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
-        // the lane's block scale (byte 2 ks + h of the row's step) moved to byte
-        // 2 (ks % 2) of its word, which op_sel picks
-        sA[i] = scales[buf][0][ra][ks / 2] >> (8u * h);
-        sB[i] = scales[buf][1][rb][ks / 2] >> (8u * h);
+      compute_ks(slot, ks, sc);
+      if (ks == 0) {
+        store_stage(slot ^ 1, s_step, S);
+        load_next();
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (ks % 2 == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                A[i], B[j], acc[i][j], 4, 4, 0, (int)sA[i], 0, (int)sB[j]);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                A[i], B[j], acc[i][j], 4, 4, 2, (int)sA[i], 2, (int)sB[j]);
-        }
     }
-    // keep the next step's LDS stores (and their wait for its loads) after this
-    // step's products
-    __builtin_amdgcn_sched_barrier(0);
-    if (step + 1 < nsteps) {
-      // the other slot was last read before the previous barrier
-      store_stage(buf ^ 1, nxt);
-      // field by field (a struct copy here ends up in scratch memory)
+#endif
+    __syncthreads();
+    if (++c_step == nsteps) {
+      if (EPI == kEpiStaged) write_tile_staged(c_tile, slot);
+      else write_tile(c_tile);
 #pragma unroll
-      for (int i = 0; i < kChunks; ++i) {
-        nxt.a[i] = far.a[i];
-        nxt.b[i] = far.b[i];
-      }
+      for (int i = 0; i < T::kTM; ++i)
 #pragma unroll
-      for (int wdx = 0; wdx < kScaleWords; ++wdx) nxt.sc[wdx] = far.sc[wdx];
-      __syncthreads();
-      buf ^= 1;
+        for (int j = 0; j < T::kTN; ++j) acc[i][j] = v16f{};
+      c_step = 0;
+      c_tile += grid;
     }
   }
-
-  // acc[i][j][r]: row 8 (r / 4) + 4 h + r % 4 of MFMA tile (i, j), column lr
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t col = n0 + wn * 64u + 32u * j + lr;
-      if (col >= N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t row = m0 + wm * 64u + 32u * i + 8u * (r >> 2) + 4u * h + (r & 3);
-        if (row >= M) continue;
-        if (OUT_BF16) {
-          const float v = acc[i][j][r];
-          // round to nearest even (finite values)
-          const uint32_t u = __float_as_uint(v);
-          const uint16_t hb = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-          // streaming stores: Y is not re-read here and must not evict the operand tiles
-          __builtin_nontemporal_store(hb, reinterpret_cast<uint16_t*>(out) + (uint64_t)row * ldo + col);
-        } else {
-          __builtin_nontemporal_store(acc[i][j][r], reinterpret_cast<float*>(out) + (uint64_t)row * ldo + col);
-        }
-      }
-    }
 }
 
 }  // namespace
 
-template <bool OUT_BF16, bool SCALE_WORDS>
-void launch_t(const GemmArgs& g, int64_t grid, int64_t tiles_n, int64_t xcd_cols) {
-  hipLaunchKernelGGL((mx_gemm_kernel<OUT_BF16, SCALE_WORDS>), dim3((unsigned)grid), dim3(256), 0,
-                     (hipStream_t)g.stream, g.qa, (uint32_t)g.lda, g.sa, (uint32_t)g.ldsa, g.qb,
-                     (uint32_t)g.ldb, g.sb, (uint32_t)g.ldsb, (uint32_t)g.M, (uint32_t)g.N,
-                     (uint32_t)g.K, g.out, (uint32_t)g.ldo, (uint32_t)tiles_n, (uint32_t)xcd_cols);
+template <class T, bool OUT_BF16, int EPI, bool SCALE_WORDS>
+void launch_t(const GemmArgs& g, int64_t tiles_n, int64_t ntiles, int64_t grid, int64_t xcd_cols) {
+  hipLaunchKernelGGL((mx_gemm_kernel<T, OUT_BF16, EPI, SCALE_WORDS>), dim3((unsigned)grid),
+                     dim3(T::kThreads), 0, (hipStream_t)g.stream, g.qa, (uint32_t)g.lda, g.sa,
+                     (uint32_t)g.ldsa, g.qb, (uint32_t)g.ldb, g.sb, (uint32_t)g.ldsb, (uint32_t)g.M,
+                     (uint32_t)g.N, (uint32_t)g.K, g.out, (uint32_t)g.ldo, (uint32_t)tiles_n,
+                     (uint32_t)ntiles, (uint32_t)xcd_cols);
+}
+
+template <class T, bool OUT_BF16, int EPI>
+void launch_w(const GemmArgs& g, bool words, int64_t tiles_n, int64_t ntiles, int64_t grid,
+              int64_t xcd_cols) {
+  if (words) launch_t<T, OUT_BF16, EPI, true>(g, tiles_n, ntiles, grid, xcd_cols);
+  else launch_t<T, OUT_BF16, EPI, false>(g, tiles_n, ntiles, grid, xcd_cols);
 }
 
 hipError_t launch_mx_gemm(const GemmArgs& g) {
-  const int64_t tiles_m = (g.M + kBM - 1) / kBM, tiles_n = (g.N + kBN - 1) / kBN;
-  const int64_t grid = tiles_m * tiles_n;
-  const int64_t xcd_cols = tiles_n % 8 == 0 ? tiles_n / 8 : 0;
+  using T = Big;
+  const int64_t tiles_m = (g.M + T::kBM - 1) / T::kBM, tiles_n = (g.N + T::kBN - 1) / T::kBN;
+  const int64_t ntiles = tiles_m * tiles_n;
+  // persistent: one workgroup per compute unit (its LDS holds one), rounded down to
+  // a multiple of 8 so that a workgroup's tiles all fall to its XCD's share
+  int64_t grid = g.cus >= 8 ? g.cus / 8 * 8 * KQ_GEMM_WG_PER_CU : 8;
+  if (grid > ntiles) grid = ntiles;
+  const int64_t xcd_cols = tiles_n % 8 == 0 && grid % 8 == 0 ? tiles_n / 8 : 0;
   // whole 32-bit scale words when every scale row starts 4-byte aligned and holds one
   const bool words = ((uintptr_t)g.sa % 4 == 0) && ((uintptr_t)g.sb % 4 == 0) && g.ldsa % 4 == 0 &&
                      g.ldsb % 4 == 0 && g.K >= 128;
+  const int64_t esize = g.out_bf16 ? 2 : 4;
+  const bool vec4 = g.N % 4 == 0 && g.ldo % 4 == 0 && (uintptr_t)g.out % (4 * esize) == 0;
+  // staged stores address a tile's rows through one buffer descriptor (below 2 GiB)
+  const bool staged = g.out_bf16 && g.N % 8 == 0 && g.ldo % 8 == 0 && (uintptr_t)g.out % 16 == 0 &&
+                      (int64_t)T::kBM * g.ldo * 2 < (int64_t(1) << 31);
   if (g.out_bf16) {
-    if (words) launch_t<true, true>(g, grid, tiles_n, xcd_cols);
-    else launch_t<true, false>(g, grid, tiles_n, xcd_cols);
+    if constexpr (T::kCanStage) {
+      if (staged) {
+        launch_w<T, true, kEpiStaged>(g, words, tiles_n, ntiles, grid, xcd_cols);
+        return hipGetLastError();
+      }
+    }
+    if (vec4) launch_w<T, true, kEpiVec4>(g, words, tiles_n, ntiles, grid, xcd_cols);
+    else launch_w<T, true, kEpiScalar>(g, words, tiles_n, ntiles, grid, xcd_cols);
   } else {
-    if (words) launch_t<false, true>(g, grid, tiles_n, xcd_cols);
-    else launch_t<false, false>(g, grid, tiles_n, xcd_cols);
+    if (vec4) launch_w<T, false, kEpiVec4>(g, words, tiles_n, ntiles, grid, xcd_cols);
+    else launch_w<T, false, kEpiScalar>(g, words, tiles_n, ntiles, grid, xcd_cols);
   }
   return hipGetLastError();
 }

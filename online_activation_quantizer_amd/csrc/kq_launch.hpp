@@ -59,6 +59,7 @@ struct GemmArgs {
   int64_t ldo;   // elements
   bool out_bf16;
   void* stream;
+  int cus;       // compute units of the device (persistent grid size)
 };
 
 inline int64_t gcd64(int64_t a, int64_t b) {

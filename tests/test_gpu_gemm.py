@@ -52,6 +52,25 @@ def test_mx_gemm_random_codes(M, N, K):
     check(host(Y), Yref, Yabs, K, f"{M}x{N}x{K}")
 
 
+def test_mx_gemm_several_tiles_per_workgroup():
+    """More 256 x 256 output tiles than workgroups (the grid is persistent and a
+    workgroup's step sequence crosses tile boundaries), ragged M and K; fp32 against
+    the reference, bf16 (four-wide stores) against the rounded fp32 result."""
+    import torch
+    M, N, K = 2321, 8192, 320
+    say(f"[mx gemm several tiles per workgroup] {M}x{N}x{K}")
+    rng = np.random.default_rng(11)
+    qa, sa = random_mx(M, K, rng)
+    qb, sb = random_mx(N, K, rng)
+    args = (dev(qa), dev(sa), dev(qb), dev(sb))
+    y32 = kq.kq_mx_gemm(*args)
+    y16 = kq.kq_mx_gemm(*args, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y32.to(torch.bfloat16), y16)
+    Yref, Yabs = oracle.mx_gemm(qa, sa, qb, sb)
+    check(host(y32), Yref, Yabs, K, f"{M}x{N}x{K}")
+
+
 def test_mx_gemm_bf16_output_is_rounded_fp32():
     import torch
     say("[mx gemm bf16]")

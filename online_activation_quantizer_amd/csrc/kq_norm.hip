@@ -14,12 +14,12 @@
 // with a stride of R x gridDim.x, loading the next row while it works on the
 // current one.
 //
-// Statistics.  Each lane takes its block's mean (pairwise sum) and sum of squared
-// deviations; the 32 lanes of a half wave are merged with the pairwise update of
-// Chan, Golub and LeVeque (count, mean, M2) by a butterfly of lane exchanges, and
-// the H half-wave partials of a row through LDS (one barrier per row), always in
-// the same order, so the result is deterministic and accurate whatever the row's
-// mean and outliers.
+// Statistics, in two passes over the row held in registers: the row sum (each
+// lane's block by pairwise addition, the 32 lanes of a half wave by a butterfly of
+// lane exchanges, the H half-wave partials of a row through LDS in a fixed order)
+// gives the mean; then the same reduction of the squared deviations from it gives
+// the variance.  Deterministic, and accurate whatever the row's mean; the
+// deviations are reused as the transform's input.
 //
 // Arithmetic.  With T_b = (kron L)(kron S) diag(d) and h = n * a + sh, where
 // n = (x - mu) * rstd and a = 1 + scale:
@@ -37,23 +37,8 @@
 namespace kq {
 namespace {
 
-// Running statistics of a set of values: count, mean, sum of squared deviations.
-struct Moments {
-  float n, mean, m2;
-};
-
-// Merge of two sets (Chan, Golub and LeVeque's pairwise update).
-__device__ __forceinline__ Moments merge(const Moments& a, const Moments& b) {
-  // branch-free: two empty sets give wb = 0 and stay empty
-  const float n = a.n + b.n;
-  const float delta = b.mean - a.mean;
-  const float wb = n > 0.0f ? b.n * __builtin_amdgcn_rcpf(n) : 0.0f;  // exact for power-of-two counts
-  return {n, __builtin_fmaf(delta, wb, a.mean), a.m2 + b.m2 + delta * delta * (a.n * wb)};
-}
-
-// Moments of one block's 32 values: pairwise sum for the mean, then the squared
-// deviations from it.
-__device__ __forceinline__ Moments block_moments(const float (&v)[kBlk]) {
+// Pairwise sum of one block's 32 values.
+__device__ __forceinline__ float block_sum(const float (&v)[kBlk]) {
   float t[kBlk / 2];
 #pragma unroll
   for (int i = 0; i < kBlk / 2; ++i) t[i] = v[2 * i] + v[2 * i + 1];
@@ -61,35 +46,21 @@ __device__ __forceinline__ Moments block_moments(const float (&v)[kBlk]) {
   for (int w = kBlk / 4; w >= 1; w >>= 1)
 #pragma unroll
     for (int i = 0; i < w; ++i) t[i] = t[2 * i] + t[2 * i + 1];
-  const float mean = t[0] * (1.0f / kBlk);
-  float m2 = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kBlk; ++i) {
-    const float dv = v[i] - mean;
-    m2 = __builtin_fmaf(dv, dv, m2);
-  }
-  return {(float)kBlk, mean, m2};
+  return t[0];
 }
 
-// Merge over the 32 lanes of a half wave (every lane ends with the same result).
-__device__ __forceinline__ Moments half_merge(Moments m) {
+// Sum over the 32 lanes of a half wave; both lanes of every exchange add the same
+// two values, so all 32 end with the same total.
+__device__ __forceinline__ float half_sum(float v) {
 #pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) {
-    const Moments o = {__shfl_xor(m.n, off), __shfl_xor(m.mean, off), __shfl_xor(m.m2, off)};
-    // both lanes of a pair merge in the same order (lower lane's set first) so they
-    // end with equal values; operands chosen by selects, not branches
-    const bool upper = (threadIdx.x & off) != 0;
-    const Moments lo = {upper ? o.n : m.n, upper ? o.mean : m.mean, upper ? o.m2 : m.m2};
-    const Moments hi = {upper ? m.n : o.n, upper ? m.mean : o.mean, upper ? m.m2 : o.m2};
-    m = merge(lo, hi);
-  }
-  return m;
+  for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
 }
 
 constexpr uint32_t kMaxNormHalves = 16;  // half waves per workgroup (512 threads: d <= 16384)
 
 template <int DT, bool MOD, bool WRITE_Y>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(3))) void norm_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(DT == DT_BF16 ? 3 : 2))) void norm_kernel(
     const uint8_t* __restrict__ x, uint32_t rows, uint32_t nb, uint32_t ldx,
     const float* __restrict__ shift, const float* __restrict__ scale, uint32_t rows_per_sample,
     float eps, float inv_d, const float* __restrict__ params, uint8_t* __restrict__ q,
@@ -97,7 +68,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(3))) void n
     uint32_t H, uint32_t R) {
   // pitches in bytes; a row takes H half waves (32 H >= nb lanes), R rows per
   // workgroup, blockDim.x = 32 H R rounded up to whole waves
-  __shared__ float part[2][kMaxNormHalves][3];
+  __shared__ float part[2][kMaxNormHalves];
   constexpr uint32_t kBlkBytes = kBlk * (DT == DT_BF16 ? 2 : 4);
   const uint32_t L = 32u * H;
   const uint32_t half = threadIdx.x >> 5;
@@ -166,28 +137,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(3))) void n
     ring = load_raw<DT>(row_ptr(rnext <= last ? rnext : rbase));
     __builtin_amdgcn_sched_barrier(0);
 
-    // row statistics: lanes, then the row's half waves (fixed order)
-    Moments m = block_moments(v);
-    if (!active) m = {0.0f, 0.0f, 0.0f};
-    m = half_merge(m);
-    if (H > 1) {
-      if ((threadIdx.x & 31u) == 0) {
-        part[buf][half][0] = m.n;
-        part[buf][half][1] = m.mean;
-        part[buf][half][2] = m.m2;
+    // row sum of the active lanes' blocks: half wave, then the row's half waves in a
+    // fixed order through LDS (two buffers: the second reduction uses the other)
+    auto row_sum = [&](float t) {
+      t = half_sum(active ? t : 0.0f);
+      if (H > 1) {
+        if ((threadIdx.x & 31u) == 0) part[buf][half] = t;
+        __syncthreads();
+        const uint32_t h0 = slot * H;
+        t = part[buf][h0];
+        for (uint32_t i = h0 + 1; i < h0 + H; ++i) t += part[buf][i];
+        buf ^= 1;
       }
-      __syncthreads();
-      const uint32_t h0 = slot * H;
-      m = {part[buf][h0][0], part[buf][h0][1], part[buf][h0][2]};
-      for (uint32_t i = h0 + 1; i < h0 + H; ++i)
-        m = merge(m, Moments{part[buf][i][0], part[buf][i][1], part[buf][i][2]});
-      buf ^= 1;
+      return t;
+    };
+    const float mean = row_sum(block_sum(v)) * inv_d;
+    float m2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i) {
+      v[i] -= mean;
+      m2 = __builtin_fmaf(v[i], v[i], m2);
     }
-    const float mean = m.mean;
-    const float rstd = __builtin_amdgcn_rsqf(m.m2 * inv_d + eps);
+    const float rstd = __builtin_amdgcn_rsqf(row_sum(m2) * inv_d + eps);
 
 #pragma unroll
-    for (int i = 0; i < kBlk; ++i) v[i] = (v[i] - mean) * k.d[i];
+    for (int i = 0; i < kBlk; ++i) v[i] *= k.d[i];
     shears<false>(v, k);
     if (MOD) {
 #pragma unroll
@@ -213,8 +187,8 @@ hipError_t launch_t(const NormArgs& n) {
   int64_t R = 256 / (32 * H);
   if (R < 1) R = 1;
   const int64_t threads = (32 * H * R + 63) / 64 * 64;
-  // about 12 resident waves per compute unit
-  int64_t per_cu = 12 / (threads / 64);
+  // the resident waves per compute unit the register budget allows (3 or 2 per SIMD)
+  int64_t per_cu = (DT == DT_BF16 ? 12 : 8) / (threads / 64);
   if (per_cu < 1) per_cu = 1;
   int64_t grid = (int64_t)a.cus * per_cu;
   const int64_t groups = (a.rows + R - 1) / R;

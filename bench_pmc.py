@@ -128,7 +128,7 @@ TRACE_KERNELS = [
     ("void kq::(anonymous namespace)::norm_kernel<0, true, false>", "`norm_kernel<bf16, modulated>` (kq_norm_quantize)"),
     ("void kq::(anonymous namespace)::butterfly_kernel<0, false, 1>",
      "`butterfly_kernel<bf16, -, weights>` (kq_quantize_weights, 12288x3072)"),
-    ("void kq::(anonymous namespace)::mx_gemm_kernel<true, true>", "`mx_gemm_kernel<bf16 out>` (kq_mx_gemm, 4608x12288x3072)"),
+    ("void kq::(anonymous namespace)::mx_gemm_kernel<", "`mx_gemm_kernel<256x256 tiles, bf16 out, staged>` (kq_mx_gemm, 4608x12288x3072)"),
     ("mlp-shape void kq::(anonymous namespace)::butterfly_kernel<0, false, 0>",
      "`butterfly_kernel<bf16, -, forward>` on 4608x12288 (the last leg)"),
     ("void at::native::(anonymous namespace)::vectorized_layer_norm_kernel", "torch layer_norm (unfused sequence)"),

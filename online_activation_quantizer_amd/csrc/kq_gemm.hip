@@ -24,10 +24,11 @@
 // advances 256 values per step (128 code bytes per row, whole cache lines): the code
 // tiles of A and B and their scale bytes are staged through LDS (two slots, code rows
 // padded by 16 bytes against bank conflicts; 152 KB), from one register stage whose
-// global loads run a step ahead.  The grid is persistent (one workgroup per compute
-// unit, tiles strided by the grid), and the step sequence runs across tile
-// boundaries: the next tile's first steps load while a tile's last step multiplies
-// and its outputs are written.  Rows past M or N are clamped on load and not stored;
+// global loads run a step ahead; its LDS stores go out one by one between the first
+// substep's products.  The grid is persistent (one workgroup per compute unit,
+// tiles strided by the grid), and the step sequence runs across tile boundaries:
+// the next tile's first steps load while a tile's last step multiplies and its
+// outputs are written.  Rows past M or N are clamped on load and not stored;
 // K-blocks past K get scale 2^-127 on both operands (their products vanish).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,12 +44,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-#ifndef KQ_GEMM_KSUB
-#define KQ_GEMM_KSUB 4
-#endif
-// 64-element K substeps (one MFMA each) per staged K step: K step = 64 KSUB values,
-// 32 KSUB code bytes per row
-constexpr int kKSub = KQ_GEMM_KSUB;
+// 64-element K substeps (one MFMA each) per staged K step: K step = 256 values, 128
+// code bytes per row
+constexpr int kKSub = 4;
 constexpr int kBKBytes = 32 * kKSub;
 constexpr int kRowChunks = kBKBytes / 16;  // 16-byte code chunks per row per step
 constexpr int kPitch = kBKBytes + 16;      // LDS code-row pitch (bank spread)
@@ -72,23 +70,8 @@ struct Tiling {
   static constexpr bool kCanStage = TN == 2 && TM % 2 == 0 && WAVES_M * WAVES_N * 64 * kPitch <= kRows * kPitch;
 };
 
-#ifndef KQ_GEMM_CFG
-#define KQ_GEMM_CFG 1
-#endif
-#if KQ_GEMM_CFG == 0
-using Big = Tiling<2, 2, 2, 2>;  // 128 x 128, 4 waves of 64 x 64
-#elif KQ_GEMM_CFG == 1
-using Big = Tiling<2, 4, 4, 2>;  // 256 x 256, 8 waves of 128 x 64
-#elif KQ_GEMM_CFG == 3
-using Big = Tiling<2, 4, 2, 2>;  // 128 x 256, 8 waves of 64 x 64
-#elif KQ_GEMM_CFG == 4
-using Big = Tiling<4, 2, 2, 2>;  // 256 x 128, 8 waves of 64 x 64
-#elif KQ_GEMM_CFG == 5
-using Big = Tiling<1, 4, 4, 2>;  // 128 x 256, 4 waves of 128 x 64
-#endif
-#ifndef KQ_GEMM_WG_PER_CU
-#define KQ_GEMM_WG_PER_CU 1
-#endif
+// 256 x 256 tiles, 8 waves of 128 x 64
+using Big = Tiling<2, 4, 4, 2>;
 
 // One K step of this thread's share of both operands, as loaded (scale words are
 // shifted and masked when stored to LDS, so no arithmetic waits on a load early).
@@ -129,15 +112,11 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   // its own L2 while the tile rows advance, and workgroups running together on an
   // XCD share their A tiles.
   auto tile_origin = [&](uint32_t t, uint32_t& m0, uint32_t& n0) {
-    uint32_t tm, tn;
-    if (xcd_cols) {
-      const uint32_t x = t & 7u, local = t >> 3;
-      tm = local / xcd_cols;
-      tn = x * xcd_cols + (local - tm * xcd_cols);
-    } else {
-      tm = t / tiles_n;
-      tn = t - tm * tiles_n;
-    }
+    // (selects, no branch: with xcd_cols = 0 this is tm = t / tiles_n, tn = t % tiles_n)
+    const uint32_t per = xcd_cols ? xcd_cols : tiles_n;
+    const uint32_t x = xcd_cols ? t & 7u : 0u, local = xcd_cols ? t >> 3 : t;
+    const uint32_t tm = local / per;
+    const uint32_t tn = x * per + (local - tm * per);
     m0 = tm * kBM;
     n0 = tn * T::kBN;
   };
@@ -174,13 +153,15 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   // operands become 0x00 (2^-127) when stored, so each of their products is below
   // 36 * 2^-254 and vanishes in the fp32 accumulation whatever the codes (E2M1 codes
   // are finite).
-  auto load_stage = [&](uint32_t step, Stage<T, SCALE_WORDS>& st) {
-    const uint32_t kb0 = step * kBKBytes;
-    const uint32_t col = 16u * (tid % kRowChunks);
-    // this thread's column in the row: past K, the row's last chunk
-    const uint32_t at = kb0 + col < kbytes ? kb0 + col : kbytes - 16u;
-#pragma unroll
-    for (int i = 0; i < T::kChunks; ++i) st.c[i] = *reinterpret_cast<const u32x4*>(code_row(i) + at);
+  // this thread's column of K step `step` in its code rows: past K, the row's last chunk
+  auto chunk_col = [&](uint32_t step) {
+    const uint32_t kb0 = step * kBKBytes, col = 16u * (tid % kRowChunks);
+    return kb0 + col < kbytes ? kb0 + col : kbytes - 16u;
+  };
+  auto load_chunk = [&](uint32_t at, int i, Stage<T, SCALE_WORDS>& st) {
+    st.c[i] = *reinterpret_cast<const u32x4*>(code_row(i) + at);
+  };
+  auto load_scales = [&](uint32_t step, Stage<T, SCALE_WORDS>& st) {
     const uint32_t blk0 = step * 2u * kKSub;  // first scale byte of this step
 #pragma unroll
     for (int j = 0; j < T::kScaleRows; ++j) {
@@ -202,12 +183,17 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
       }
     }
   };
-  auto store_stage = [&](int slot, uint32_t step, const Stage<T, SCALE_WORDS>& st) {
+  auto load_stage = [&](uint32_t step, Stage<T, SCALE_WORDS>& st) {
+    const uint32_t at = chunk_col(step);
 #pragma unroll
-    for (int i = 0; i < T::kChunks; ++i) {
-      const uint32_t c = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(&codes[slot][(c / kRowChunks) * kPitch + (c % kRowChunks) * 16u]) = st.c[i];
-    }
+    for (int i = 0; i < T::kChunks; ++i) load_chunk(at, i, st);
+    load_scales(step, st);
+  };
+  auto store_chunk = [&](int slot, int i, const Stage<T, SCALE_WORDS>& st) {
+    const uint32_t c = tid + kThreads * i;
+    *reinterpret_cast<u32x4*>(&codes[slot][(c / kRowChunks) * kPitch + (c % kRowChunks) * 16u]) = st.c[i];
+  };
+  auto store_scales = [&](int slot, uint32_t step, const Stage<T, SCALE_WORDS>& st) {
     const uint32_t blk0 = step * 2u * kKSub;
 #pragma unroll
     for (int j = 0; j < T::kScaleRows; ++j) {
@@ -229,6 +215,11 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
         if (kRows % kThreads == 0 || r < (uint32_t)kRows) scales[slot][r][wdx] = w & keep;  // past K: 0x00
       }
     }
+  };
+  auto store_stage = [&](int slot, uint32_t step, const Stage<T, SCALE_WORDS>& st) {
+#pragma unroll
+    for (int i = 0; i < T::kChunks; ++i) store_chunk(slot, i, st);
+    store_scales(slot, step, st);
   };
 
   // acc[i][j]: the wave's A row tile i (32 rows of Y) times its B row tile j (32
@@ -258,8 +249,8 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
       for (int w = 0; w < kScaleWords; ++w) sc.b[j][w] = scales[slot][r][w];
     }
   };
-  // the products of one 64-wide K substep
-  auto compute_ks = [&](int slot, int ks, const Scales& sc) {
+  // the products of one 64-wide K substep; after_mfma(u, acc) runs after the u-th
+  auto compute_ks = [&](int slot, int ks, const Scales& sc, auto&& after_mfma) {
     v8i A[T::kTM], B[T::kTN];
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) {
@@ -284,8 +275,10 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(B[j], A[i], acc[i][j], 4, 4, 0, sB, 0, sA);
         else
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(B[j], A[i], acc[i][j], 4, 4, 2, sB, 2, sA);
+        after_mfma(i * T::kTN + j, acc[i][j]);
       }
   };
+  auto no_hook = [](int, const v16f&) {};
 
   // acc[i][j][4 q + e]: Y row lr of the wave's A tile i, column 8 q + 4 h + e of its
   // B tile j
@@ -399,14 +392,18 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   set_rows(l_tile);
   Stage<T, SCALE_WORDS> S;
   uint32_t s_step = 0;  // K step held in S
+  // (branch-free, so that the step's products, LDS stores and loads stay in one
+  // block the scheduler can interleave; past the last tile the last tile's rows)
+  auto advance = [&]() {
+    const bool wrap = l_step + 1u == nsteps;
+    l_step = wrap ? 0u : l_step + 1u;
+    l_tile = wrap ? l_tile + grid : l_tile;
+    set_rows(l_tile < ntiles ? l_tile : ntiles - 1u);
+  };
   auto load_next = [&]() {
     s_step = l_step;
     load_stage(l_step, S);
-    if (++l_step == nsteps) {
-      l_step = 0;
-      l_tile += grid;
-      if (l_tile < ntiles) set_rows(l_tile);
-    }
+    advance();
   };
   load_next();
   store_stage(0, s_step, S);
@@ -417,31 +414,21 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
     const int slot = (int)(g & 1u);
     Scales sc;
     read_scales(slot, sc);
-#ifndef KQ_GEMM_PINGPONG
-#define KQ_GEMM_PINGPONG 0
+    // The stores of S into the other slot go one by one between the first substep's
+    // products (the empty asm takes the product just issued, and its memory clobber
+    // keeps the store after it), then the loads of the step after next start.
+    compute_ks(slot, 0, sc, [&](int u, const v16f& a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+      asm volatile("" ::"v"(a) : "memory");
 #endif
-#if KQ_GEMM_PINGPONG
-    const bool early = wave >= (uint32_t)(kThreads / 128);  // second half of the waves
-    if (early) {
-      store_stage(slot ^ 1, s_step, S);
-      load_next();
-    }
+      if (u < T::kChunks) store_chunk(slot ^ 1, u, S);
+    });
 #pragma unroll
-    for (int ks = 0; ks < kKSub; ++ks) compute_ks(slot, ks, sc);
-    if (!early) {
-      store_stage(slot ^ 1, s_step, S);
-      load_next();
-    }
-#else
+    for (int i = T::kTM * T::kTN; i < T::kChunks; ++i) store_chunk(slot ^ 1, i, S);
+    store_scales(slot ^ 1, s_step, S);
+    load_next();
 #pragma unroll
-    for (int ks = 0; ks < kKSub; ++ks) {
-      compute_ks(slot, ks, sc);
-      if (ks == 0) {
-        store_stage(slot ^ 1, s_step, S);
-        load_next();
-      }
-    }
-#endif
+    for (int ks = 1; ks < kKSub; ++ks) compute_ks(slot, ks, sc, no_hook);
     __syncthreads();
     if (++c_step == nsteps) {
       if (EPI == kEpiStaged) write_tile_staged(c_tile, slot);
@@ -480,7 +467,7 @@ hipError_t launch_mx_gemm(const GemmArgs& g) {
   const int64_t ntiles = tiles_m * tiles_n;
   // persistent: one workgroup per compute unit (its LDS holds one), rounded down to
   // a multiple of 8 so that a workgroup's tiles all fall to its XCD's share
-  int64_t grid = g.cus >= 8 ? g.cus / 8 * 8 * KQ_GEMM_WG_PER_CU : 8;
+  int64_t grid = g.cus >= 8 ? g.cus / 8 * 8 : 8;
   if (grid > ntiles) grid = ntiles;
   const int64_t xcd_cols = tiles_n % 8 == 0 && grid % 8 == 0 ? tiles_n / 8 : 0;
   // whole 32-bit scale words when every scale row starts 4-byte aligned and holds one

@@ -49,12 +49,29 @@ __device__ __forceinline__ float block_sum(const float (&v)[kBlk]) {
   return t[0];
 }
 
-// Sum over the 32 lanes of a half wave; both lanes of every exchange add the same
-// two values, so all 32 end with the same total.
+// v + the value DPP control CTRL moves into this lane (quad permutations and row
+// mirrors within rows of 16 lanes, a row's last lane broadcast to the next row);
+// rows outside ROW_MASK keep v.  One v_add_f32_dpp.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float add_dpp(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                  ROW_MASK, 0xF, false));
+}
+
+// Sum over the 32 lanes of a half wave: exchanges with the partner lane in the quad
+// (xor 1, xor 2) and the mirrored lane in the half row and in the row leave every
+// lane of a row with the row's total; the first row's total is then added into the
+// second row (row broadcast), and lane 31 (63) holds the half wave's total, which
+// every lane of that half reads.  One summation order for all 32 lanes.
 __device__ __forceinline__ float half_sum(float v) {
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v = add_dpp<0xB1>(v);         // quad_perm [1,0,3,2]
+  v = add_dpp<0x4E>(v);         // quad_perm [2,3,0,1]
+  v = add_dpp<0x141>(v);        // row_half_mirror
+  v = add_dpp<0x140>(v);        // row_mirror
+  v = add_dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+  const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  return (threadIdx.x & 32u) ? t1 : t0;
 }
 
 constexpr uint32_t kMaxNormHalves = 16;  // half waves per workgroup (512 threads: d <= 16384)

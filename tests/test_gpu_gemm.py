@@ -71,6 +71,28 @@ def test_mx_gemm_several_tiles_per_workgroup():
     check(host(y32), Yref, Yabs, K, f"{M}x{N}x{K}")
 
 
+def test_mx_gemm_several_tiles_byte_scales_and_odd_n():
+    """The persistent grid's other paths: scale rows read byte by byte (K below 128,
+    scale pointer and pitch not word-aligned) and N not a multiple of 4 (one output
+    per store), with more tiles than workgroups."""
+    import torch
+    M, N, K = 2100, 8190, 96
+    say(f"[mx gemm byte scales, odd N] {M}x{N}x{K}")
+    rng = np.random.default_rng(12)
+    qa, sa_full = random_mx(M, K + 32, rng)   # one spare block per row: pitch 4, data at byte 1
+    qb, sb_full = random_mx(N, K + 32, rng)
+    qa, qb = np.ascontiguousarray(qa[:, :K // 2]), np.ascontiguousarray(qb[:, :K // 2])
+    sa_d, sb_d = dev(sa_full)[:, 1:1 + K // 32], dev(sb_full)[:, 1:1 + K // 32]
+    args = (dev(qa), sa_d, dev(qb), sb_d)
+    y32 = kq.kq_mx_gemm(*args)
+    y16 = kq.kq_mx_gemm(*args, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y32.to(torch.bfloat16), y16)
+    sa, sb = np.ascontiguousarray(sa_full[:, 1:1 + K // 32]), np.ascontiguousarray(sb_full[:, 1:1 + K // 32])
+    Yref, Yabs = oracle.mx_gemm(qa, sa, qb, sb)
+    check(host(y32), Yref, Yabs, K, f"{M}x{N}x{K}")
+
+
 def test_mx_gemm_bf16_output_is_rounded_fp32():
     import torch
     say("[mx gemm bf16]")

@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--pool", type=int, default=16, help="distinct buffer sets rotated over")
+    ap.add_argument("--pool", type=int, default=32, help="distinct buffer sets rotated over (1.15 GB at 32)")
     ap.add_argument("--variant", choices=["butterfly", "mfma"], default="butterfly")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-sq", action="store_true",

@@ -163,10 +163,11 @@ def trace(trace_dir, bench_json):
     md = ["# Kernel trace of bench.py, FLUX.1-schnell-like 4608x3072 bf16 workload (one MI355X)", "",
           "Commands (repository root):", "", "```",
           "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o bench -- python3 bench.py --no-cpu --no-sweep",
-          "python3 bench.py > out/bench.json",
+          "python3 bench.py --no-cpu --no-sweep > out/bench.json",
           "python3 bench_pmc.py trace out/trace out/bench.json", "```", "",
-          "bench.py replays each timed leg from one captured HIP graph (16 rotating buffer sets for the "
-          "4608x3072 legs).  Durations from the trace (end - start per dispatch), microseconds:", "",
+          "bench.py replays each timed leg from one captured HIP graph (%d rotating buffer sets for the "
+          "4608x3072 legs).  Durations from the trace (end - start per dispatch), microseconds:"
+          % b.get("config", {}).get("pool_sets", 0), "",
           "| kernel | dispatches | average | median | p10 | p90 |", "|---|---|---|---|---|---|"]
     kq_avg = None
     for prefix, label in TRACE_KERNELS:

@@ -190,8 +190,10 @@ int hq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_
  *   eps              >= 0, finite (KQ_ERR_VALUE otherwise)
  *   params           device float32 [d/32][5][3] (KQ_T_PARAMS format)
  * d is at most 16384 here (one row per workgroup; KQ_ERR_SHAPE beyond).
- * Computed in fp32: per-block moments merged pairwise for the statistics, the
- * modulation folded into the transform's diagonal plus a constant T_b shift.
+ * Computed in fp32: the row mean from a sum reduction, then the variance from the
+ * same reduction of the squared deviations (both in a fixed order, so the result
+ * is deterministic); the modulation folded into the transform's diagonal plus a
+ * constant T_b shift.
  * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_DTYPE, KQ_ERR_VALUE, KQ_ERR_HIP. */
 int kq_norm_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
                      const float* shift, const float* scale, int64_t rows_per_sample, float eps,

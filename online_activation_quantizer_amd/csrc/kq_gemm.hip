@@ -387,7 +387,7 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   // unconditionally (past the last step of the last tile, the last tile's rows are
   // re-read), so the only wait for memory is the one before S goes to LDS.
   const uint32_t my_tiles = (ntiles - 1u - blockIdx.x) / grid + 1u;  // grid <= ntiles
-  const uint32_t total = my_tiles * nsteps;
+  const uint64_t total = (uint64_t)my_tiles * nsteps;
   uint32_t l_tile = blockIdx.x, l_step = 0;  // the step the next load fetches
   set_rows(l_tile);
   Stage<T, SCALE_WORDS> S;
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   load_next();
   __syncthreads();
   uint32_t c_tile = blockIdx.x, c_step = 0;
-  for (uint32_t g = 0; g < total; ++g) {
+  for (uint64_t g = 0; g < total; ++g) {
     const int slot = (int)(g & 1u);
     Scales sc;
     read_scales(slot, sc);

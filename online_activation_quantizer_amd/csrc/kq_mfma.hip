@@ -21,9 +21,12 @@
 // it in LDS (double-buffered, 528-byte row pitch so the 32 rows of a column fall
 // on distinct banks) and each wave reads its two blocks' MFMA operands back with
 // ds_read_b128.  The 12 A operands of a wave's two blocks stay in VGPRs for the
-// whole walk.  Rows past the end and blocks past nb are clamped to the last row /
-// block: those lanes recompute and re-store exactly the bytes of the lane that
-// owns them, so no memory operation is predicated.
+// whole walk.  The code bytes of a tile are staged in LDS and leave as whole
+// 128-byte row segments (written straight from the lanes they would be 16-byte
+// pieces of 32 rows per instruction, partial lines).  Rows past the end and blocks
+// past nb are clamped to the last row / block: those lanes recompute and re-store
+// exactly the bytes of the lane that owns them, so no memory operation is
+// predicated.
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
@@ -35,6 +38,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTileRows = 32;
 constexpr int kTileBlocks = 8;                    // 2 per wave
@@ -42,9 +46,13 @@ constexpr int kChunksPerRow = kTileBlocks * 4;    // 16-byte chunks per tile row
 constexpr int kPitch = kTileBlocks * 64 + 16;     // LDS row pitch in bytes
 constexpr int kTileBytes = kTileRows * kPitch;
 constexpr int kChunksPerThread = kTileRows * kChunksPerRow / kThreads;  // 4
+constexpr int kQPitch = kTileBlocks * 16 + 16;    // staged code row: 128 bytes + 16
+static_assert(kTileRows * kTileBlocks * 16 == kThreads * 16, "one 16-byte code store per thread");
 
 constexpr int kMfmaBlocksPerCU = 3;  // resident workgroups per CU (LDS: 33 KB each)
 
+// Encodes one block of one token (this lane's half of it): the 16 code bytes go to
+// the workgroup's staging row `qrow` in LDS, the scale byte straight to memory.
 template <bool WRITE_Y>
 __device__ __forceinline__ void encode_tile(floatx16 acc, int h, uint8_t* qrow, uint8_t* srow,
                                             float* yrow) {
@@ -87,7 +95,7 @@ __device__ __forceinline__ void encode_tile(floatx16 acc, int h, uint8_t* qrow, 
   if (h == 0) *srow = (uint8_t)S;
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 template <bool WRITE_Y>
 __global__ __launch_bounds__(kThreads) void mfma_kernel(
@@ -95,6 +103,8 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
     const uint16_t* __restrict__ T3, uint8_t* __restrict__ q, int64_t ldq,
     uint8_t* __restrict__ s, int64_t lds, float* __restrict__ y, int64_t ldy, uint32_t tstep) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTileBytes];
+  // the tile's code bytes, 32 rows of the group's 8 blocks (16 bytes each), padded
+  __shared__ __attribute__((aligned(16))) uint8_t qstage[kTileRows][kQPitch];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
@@ -112,13 +122,15 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
   if (cblk > nb - 1) cblk = nb - 1;
   const int64_t ccol_elem = (int64_t)cblk * kBlk + (ccol & 3) * 8;
   const int crow0 = tid / kChunksPerRow;
-  uint4 R[kChunksPerThread];
+  // (register-friendly vector type: an array of HIP's uint4 struct ends up in
+  // scratch memory, each load waited for at once)
+  u32x4 R[kChunksPerThread];
   auto load_tile = [&](uint32_t t_idx) {
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
       int64_t row = (int64_t)t_idx * kTileRows + crow0 + 8 * i;
       row = row < last ? row : last;
-      R[i] = *reinterpret_cast<const uint4*>(x + row * ldx + ccol_elem);
+      R[i] = *reinterpret_cast<const u32x4*>(x + row * ldx + ccol_elem);
     }
   };
   load_tile(rt);
@@ -142,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
   for (;;) {
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i)
-      *reinterpret_cast<uint4*>(&tile[buf][(crow0 + 8 * i) * kPitch + ccol * 16]) = R[i];
+      *reinterpret_cast<u32x4*>(&tile[buf][(crow0 + 8 * i) * kPitch + ccol * 16]) = R[i];
     __syncthreads();
     const uint32_t rn = rt + tstep;
     // next tile in flight during the math (clamped: the last pass re-reads a valid tile)
@@ -154,8 +166,8 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
     for (int j = 0; j < 2; ++j) {
       const int jb = 2 * wave + j;
       const uint8_t* src = &tile[buf][n * kPitch + jb * 64 + 16 * h];
-      const bf16x8 B0 = as_bf16x8(*reinterpret_cast<const uint4*>(src));
-      const bf16x8 B1 = as_bf16x8(*reinterpret_cast<const uint4*>(src + 32));
+      const bf16x8 B0 = as_bf16x8(*reinterpret_cast<const u32x4*>(src));
+      const bf16x8 B1 = as_bf16x8(*reinterpret_cast<const u32x4*>(src + 32));
       floatx16 acc = {};
       // smallest parts first
 #pragma unroll
@@ -163,8 +175,21 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[j][sp][0], B0, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[j][sp][1], B1, acc, 0, 0, 0);
       }
-      encode_tile<WRITE_Y>(acc, h, q + t * ldq + 16 * blk[j], s + t * lds + blk[j],
+      encode_tile<WRITE_Y>(acc, h, &qstage[n][16 * jb], s + t * lds + blk[j],
                            WRITE_Y ? y + t * ldy + 32 * blk[j] : nullptr);
+    }
+    __syncthreads();
+    // the tile's codes leave as whole 128-byte row segments: 8 threads per row, each
+    // 16 bytes (rows past the end and blocks past nb hold exactly the bytes of the
+    // last row / block, and are written there again)
+    {
+      const int sr = tid >> 3, sc = tid & 7;
+      int64_t row = (int64_t)rt * kTileRows + sr;
+      row = row < last ? row : last;
+      uint32_t b = bg * kTileBlocks + sc;
+      b = b < nb ? b : nb - 1;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&qstage[sr][16 * sc]);
+      *reinterpret_cast<u32x4*>(q + row * ldq + 16 * b) = v;
     }
     if (rn >= ntiles) return;
     rt = rn;

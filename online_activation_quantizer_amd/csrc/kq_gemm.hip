@@ -71,7 +71,7 @@ struct Tiling {
 };
 
 // 256 x 256 tiles, 8 waves of 128 x 64
-using Big = Tiling<2, 4, 4, 2>;
+using ProductTiling = Tiling<2, 4, 4, 2>;
 
 // One K step of this thread's share of both operands, as loaded (scale words are
 // shifted and masked when stored to LDS, so no arithmetic waits on a load early).
@@ -462,7 +462,7 @@ void launch_w(const GemmArgs& g, bool words, int64_t tiles_n, int64_t ntiles, in
 }
 
 hipError_t launch_mx_gemm(const GemmArgs& g) {
-  using T = Big;
+  using T = ProductTiling;
   const int64_t tiles_m = (g.M + T::kBM - 1) / T::kBM, tiles_n = (g.N + T::kBN - 1) / T::kBN;
   const int64_t ntiles = tiles_m * tiles_n;
   // persistent: one workgroup per compute unit (its LDS holds one), rounded down to

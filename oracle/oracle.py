@@ -2,8 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY.  Each function mirrors one C entry point; the
 arithmetic lives in the C++ file, whose header names the passages it follows.
-Parity unpinned: nothing on the pages prints numeric values for this path, so
-the oracle is pinned by closed forms, invariants and brute force in the tests.
+The pages print no numeric worked example for this path, so every function is
+pinned by closed forms, invariants, brute force and hand-derived examples in the
+tests.
 """
 from __future__ import annotations
 

@@ -9,12 +9,14 @@
 // then y_b = T_b h_b per 32-channel block and the MXFP4 encoding of y.
 //
 // Mapping.  A row is handled by H = ceil(nb / 32) half waves, one lane per block
-// (lanes past nb idle), and a workgroup holds R = max(1, 256 / 32H) rows packed
-// back to back, so every lane keeps one block for the whole kernel and walks rows
-// with a stride of R x gridDim.x, loading the next row while it works on the
-// current one.
+// (lanes past nb idle), and a workgroup holds R = max(1, 256 / 32H) row slots
+// packed back to back, so every lane keeps one block for the whole kernel.  Each
+// lane carries two rows at a time, slot s of rows rbase + s and rbase + R + s, and
+// walks on with a stride of 2R x gridDim.x, loading its next two rows while it
+// works on the current ones: the two rows' reductions share their LDS round trips
+// and barriers, and their arithmetic fills each other's waits.
 //
-// Statistics, in two passes over the row held in registers: the row sum (each
+// Statistics, in two passes over the rows held in registers: the row sum (each
 // lane's block by pairwise addition, the 32 lanes of a half wave by a butterfly of
 // lane exchanges, the H half-wave partials of a row through LDS in a fixed order)
 // gives the mean; then the same reduction of the squared deviations from it gives
@@ -77,15 +79,14 @@ __device__ __forceinline__ float half_sum(float v) {
 constexpr uint32_t kMaxNormHalves = 16;  // half waves per workgroup (512 threads: d <= 16384)
 
 template <int DT, bool MOD, bool WRITE_Y>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(DT == DT_BF16 ? 3 : 2))) void norm_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void norm_kernel(
     const uint8_t* __restrict__ x, uint32_t rows, uint32_t nb, uint32_t ldx,
     const float* __restrict__ shift, const float* __restrict__ scale, uint32_t rows_per_sample,
     float eps, float inv_d, const float* __restrict__ params, uint8_t* __restrict__ q,
     uint32_t ldq, uint8_t* __restrict__ s, uint32_t lds, float* __restrict__ y, uint32_t ldy,
     uint32_t H, uint32_t R) {
-  // pitches in bytes; a row takes H half waves (32 H >= nb lanes), R rows per
+  // pitches in bytes; a row takes H half waves (32 H >= nb lanes), R row slots per
   // workgroup, blockDim.x = 32 H R rounded up to whole waves
-  __shared__ float part[2][kMaxNormHalves];
   constexpr uint32_t kBlkBytes = kBlk * (DT == DT_BF16 ? 2 : 4);
   const uint32_t L = 32u * H;
   const uint32_t half = threadIdx.x >> 5;
@@ -94,20 +95,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(DT == DT_BF
   const uint32_t slot = slot0 < R ? slot0 : R - 1;
   const uint32_t bb = b < nb ? b : nb - 1;  // idle lanes shadow a real block, store nothing
   const uint32_t last = rows - 1;
-  const uint32_t rstep = gridDim.x * R;
   const uint64_t d = (uint64_t)nb * kBlk;
   const uint8_t* const xcol = x + (uint64_t)bb * kBlkBytes;
 
-  // rows of this lane: r0 + k * rstep; the workgroup iterates while its first slot's
-  // row exists, so every wave reaches every barrier (rows past the end are clamped
-  // and not stored)
-  uint32_t rbase = blockIdx.x * R;
+  // half-wave partials of the two rows, two buffers (consecutive reductions
+  // alternate, so a fast wave never overwrites partials a slow one still reads)
+  __shared__ float part[2][2 * kMaxNormHalves];
+  // the lane's rows: rbase + slot and rbase + R + slot, rbase advancing by 2R x
+  // gridDim.x; the workgroup iterates while its first row exists, so every wave
+  // reaches every barrier (rows past the end are clamped and not stored)
+  uint32_t rbase = blockIdx.x * 2u * R;
   if (rbase > last) return;  // uniform over the workgroup
-  auto row_ptr = [&](uint32_t rb) {
-    const uint32_t r = rb + slot;
-    return xcol + (uint64_t)(r < last ? r : last) * ldx;
-  };
-  Raw<DT> ring = load_raw<DT>(row_ptr(rbase));
+  const uint32_t rstep = gridDim.x * 2u * R;
+  auto row_ptr = [&](uint32_t r) { return xcol + (uint64_t)(r < last ? r : last) * ldx; };
+  Raw<DT> ringA = load_raw<DT>(row_ptr(rbase + slot));
+  Raw<DT> ringB = load_raw<DT>(row_ptr(rbase + R + slot));
 
   // per-lane constants: shear coefficients, the modulated diagonal e and c = T_b shift
   // (rebuilt from the factors whenever the lane's row moves to another sample)
@@ -141,42 +143,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(DT == DT_BF
   };
 
   int buf = 0;
-  for (;;) {
-    const uint32_t r = rbase + slot;
-    const bool store = active && r <= last;
-    const uint32_t rr = r < last ? r : last;
-    // constants first, while only the prefetched row is live
-    const uint64_t g = MOD ? rr / rows_per_sample : 0;
-    if (g != cur_g) set_sample(g);
-    float v[kBlk];
-    unpack(ring, v);
-    const uint32_t rnext = rbase + rstep;
-    ring = load_raw<DT>(row_ptr(rnext <= last ? rnext : rbase));
-    __builtin_amdgcn_sched_barrier(0);
-
-    // row sum of the active lanes' blocks: half wave, then the row's half waves in a
-    // fixed order through LDS (two buffers: the second reduction uses the other)
-    auto row_sum = [&](float t) {
-      t = half_sum(active ? t : 0.0f);
-      if (H > 1) {
-        if ((threadIdx.x & 31u) == 0) part[buf][half] = t;
-        __syncthreads();
-        const uint32_t h0 = slot * H;
-        t = part[buf][h0];
-        for (uint32_t i = h0 + 1; i < h0 + H; ++i) t += part[buf][i];
-        buf ^= 1;
+  // row sums of both rows: each half wave's, then the row's half waves in a fixed
+  // order through LDS
+  auto row_sum2 = [&](float& ta, float& tb) {
+    ta = half_sum(active ? ta : 0.0f);
+    tb = half_sum(active ? tb : 0.0f);
+    if (H > 1) {
+      if ((threadIdx.x & 31u) == 0) {
+        part[buf][half] = ta;
+        part[buf][kMaxNormHalves + half] = tb;
       }
-      return t;
-    };
-    const float mean = row_sum(block_sum(v)) * inv_d;
-    float m2 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kBlk; ++i) {
-      v[i] -= mean;
-      m2 = __builtin_fmaf(v[i], v[i], m2);
+      __syncthreads();
+      const uint32_t h0 = slot * H;
+      ta = part[buf][h0];
+      tb = part[buf][kMaxNormHalves + h0];
+      for (uint32_t i = h0 + 1; i < h0 + H; ++i) {
+        ta += part[buf][i];
+        tb += part[buf][kMaxNormHalves + i];
+      }
+      buf ^= 1;
     }
-    const float rstd = __builtin_amdgcn_rsqf(row_sum(m2) * inv_d + eps);
-
+  };
+  // the transform, rstd and the modulation constant, then the encoder
+  auto finish = [&](float (&v)[kBlk], float rstd, uint32_t r, bool store) {
 #pragma unroll
     for (int i = 0; i < kBlk; ++i) v[i] *= k.d[i];
     shears<false>(v, k);
@@ -192,6 +181,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(DT == DT_BF
         store_y(reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(y) + (uint64_t)r * ldy) + b * kBlk, v);
       encode_store(v, q + (uint64_t)r * ldq + b * (kBlk / 2), s + (uint64_t)r * lds + b);
     }
+  };
+
+  for (;;) {
+    const uint32_t ra = rbase + slot, rb = rbase + R + slot;
+    const uint32_t raa = ra < last ? ra : last, rbb = rb < last ? rb : last;
+    const bool storeA = active && ra <= last, storeB = active && rb <= last;
+    const uint64_t ga = MOD ? raa / rows_per_sample : 0, gb = MOD ? rbb / rows_per_sample : 0;
+    float va[kBlk], vb[kBlk];
+    unpack(ringA, va);
+    unpack(ringB, vb);
+    const uint32_t rnext = rbase + rstep;
+    const uint32_t rn = rnext <= last ? rnext : rbase;
+    // the next two rows in flight during the math (the last pass re-reads valid rows)
+    ringA = load_raw<DT>(row_ptr(rn + slot));
+    ringB = load_raw<DT>(row_ptr(rn + R + slot));
+    __builtin_amdgcn_sched_barrier(0);
+    // statistics of both rows first (no per-sample constants involved), then each
+    // row's transform with its sample's constants
+    float sa = block_sum(va), sb = block_sum(vb);
+    row_sum2(sa, sb);
+    const float ma = sa * inv_d, mb = sb * inv_d;
+    float m2a = 0.0f, m2b = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i) {
+      va[i] -= ma;
+      m2a = __builtin_fmaf(va[i], va[i], m2a);
+      vb[i] -= mb;
+      m2b = __builtin_fmaf(vb[i], vb[i], m2b);
+    }
+    row_sum2(m2a, m2b);
+    const float rsa = __builtin_amdgcn_rsqf(m2a * inv_d + eps);
+    const float rsb = __builtin_amdgcn_rsqf(m2b * inv_d + eps);
+    if (ga != cur_g) set_sample(ga);
+    finish(va, rsa, ra, storeA);
+    if (gb != cur_g) set_sample(gb);
+    finish(vb, rsb, rb, storeB);
     if (rnext > last) return;  // uniform over the workgroup
     rbase = rnext;
   }
@@ -204,11 +229,11 @@ hipError_t launch_t(const NormArgs& n) {
   int64_t R = 256 / (32 * H);
   if (R < 1) R = 1;
   const int64_t threads = (32 * H * R + 63) / 64 * 64;
-  // the resident waves per compute unit the register budget allows (3 or 2 per SIMD)
-  int64_t per_cu = (DT == DT_BF16 ? 12 : 8) / (threads / 64);
+  // the resident waves per compute unit the register budget allows (2 per SIMD)
+  int64_t per_cu = 8 / (threads / 64);
   if (per_cu < 1) per_cu = 1;
   int64_t grid = (int64_t)a.cus * per_cu;
-  const int64_t groups = (a.rows + R - 1) / R;
+  const int64_t groups = (a.rows + 2 * R - 1) / (2 * R);  // 2R rows per workgroup pass
   if (grid > groups) grid = groups;
   const int64_t esz = DT == DT_BF16 ? 2 : 4;
   hipLaunchKernelGGL((norm_kernel<DT, MOD, WRITE_Y>), dim3((unsigned)grid), dim3((unsigned)threads),

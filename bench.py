@@ -8,8 +8,10 @@ resident in HBM before the timed region; the steps rotate through a pool of
 distinct input/output buffer sets larger than the 256 MB last-level cache, so
 every step reads its activations from HBM rather than from cache.
 
-Prints one JSON line.  Extra keys beside the contract: the SmoothQuant baseline
-timed the same way, and a parity summary of one step against the oracle.
+Prints one JSON line.  Extra keys beside the contract: the SmoothQuant and
+Hadamard baselines timed the same way, the other kernels' legs, one GPU's share
+at 8-way sharding, and (in the CPU leg, the only part that runs the oracle) a
+parity summary of one step against it.
 """
 import argparse
 import json
@@ -41,6 +43,7 @@ def parse():
     ap.add_argument("--no-weights", action="store_true", help="skip the weight-side timing")
     ap.add_argument("--no-gemm", action="store_true", help="skip the W4A4 product timing")
     ap.add_argument("--no-mlp", action="store_true", help="skip the 4608x12288 quantizer timing")
+    ap.add_argument("--no-shard", action="store_true", help="skip the 8-way shard timing")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the 28-call batched sweep (14 x 18432x3072 + 14 x 18432x12288)")
     ap.add_argument("--no-norm", action="store_true",
@@ -242,6 +245,42 @@ def mlp_timing(args):
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def shard_timing(args, xs, ps):
+    """One GPU's share of the FLUX layer at 8-way sharding, each call on its own
+    buffers from a pool larger than the last-level cache: token shards X[576, 3072]
+    (all 96 factor sets; contiguous row ranges of the pool's inputs) and channel
+    shards X[4608, 384] (12 factor sets; contiguous copies of column ranges)."""
+    import torch
+
+    import online_activation_quantizer_amd as kq
+    rows, d = xs[0].shape
+    nb = d // 32
+    P = len(xs)
+    out = {"workload": f"one GPU's share of {rows}x{d} bf16 at 8-way sharding"}
+    legs = {
+        "token_shard": [(x[r:r + rows // 8], p) for x, p in zip(xs, ps) for r in range(0, rows, rows // 8)],
+        "channel_shard": [(xs[i % P][:, (i // P % 8) * (d // 8):(i // P % 8 + 1) * (d // 8)].contiguous(),
+                           ps[i % P][(i // P % 8) * (nb // 8):(i // P % 8 + 1) * (nb // 8)].contiguous())
+                          for i in range(min(8 * P, 96))],
+    }
+    for name, sets in legs.items():
+        qs = [torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.uint8, device="cuda") for x, _ in sets]
+        ss = [torch.empty((x.shape[0], x.shape[1] // 32), dtype=torch.uint8, device="cuda") for x, _ in sets]
+
+        def step(i, sets=sets, qs=qs, ss=ss):
+            j = i % len(sets)
+            kq.kq_quantize(sets[j][0], sets[j][1], q=qs[j], s=ss[j])
+
+        ms = (timed(step, args.steps, args.warmup, torch.cuda.current_stream()) if args.eager
+              else timed_graph(step, args.steps, args.warmup))
+        elems = sets[0][0].numel()
+        gbs = elems * BYTES_PER_ELEM / (ms * 1e-3) / 1e9
+        out[name] = {"shape": list(sets[0][0].shape), "distinct_sets": len(sets), "us_per_call": round(ms * 1e3, 3),
+                     "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        del qs, ss
+    return out
+
+
 def sweep_timing(args):
     """The batched sweep: 28 layer-shaped calls alternating X[18432, 3072] and
     X[18432, 12288] bf16, each with its own inputs, factor set and outputs (10 GB moved,
@@ -342,6 +381,25 @@ def weights_timing(args):
             "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def cpu_leg(x0, p0, q0, s0, seconds):
+    """The CPU leg, the only part of the bench that runs the oracle: the oracle timed
+    on the host cores (cpu_baseline), the other rows' oracles on bounded samples,
+    and the classification of one production step's output (q0, s0) against it."""
+    out = {"cpu_baseline": cpu_baseline(x0, p0, seconds)}
+    try:
+        out["cpu_oracles"] = cpu_oracles(x0, p0, out["cpu_baseline"]["cores"])
+    except Exception as e:  # the oracle is test infrastructure; its absence does not stop timing
+        out["cpu_oracles"] = {"error": str(e)}
+    try:
+        import oracle
+        _, _, y_o = oracle.quantize(x0, p0, want_y=True)
+        st = oracle.classify(x0, y_o, q0, s0, 0, 1e-5)
+        out["parity"] = {k: st[k] for k in ("exact", "excused", "unexcused", "elements")}
+    except Exception as e:
+        out["parity"] = {"error": str(e)}
+    return out
+
+
 def cpu_oracles(x0, p0, threads):
     """The oracle of every other row timed on bounded samples of the same workloads
     (host cores; about a second each), reported beside the GPU figures."""
@@ -437,20 +495,9 @@ def main():
     norm = None if args.no_norm else norm_timing(args, cfg, xs, ps, qs, ss, ms)
     gemm = None if args.no_gemm else gemm_timing(args, qs, ss)
     mlp = None if args.no_mlp else mlp_timing(args)
+    shard = None if args.no_shard or args.variant != "butterfly" else shard_timing(args, xs, ps)
     sweep = None if args.no_sweep else sweep_timing(args)
     ceiling = None if args.no_ceiling else stream_ceiling(args, xs, qs, ss, ms)
-
-    # parity of one production step against the oracle
-    parity = None
-    try:
-        import oracle
-        kq_step(0)
-        torch.cuda.synchronize()
-        _, _, y_o = oracle.quantize(x0, p0, want_y=True)
-        st = oracle.classify(x0, y_o, qs[0].cpu().numpy(), ss[0].cpu().numpy(), 0, 1e-5)
-        parity = {k: st[k] for k in ("exact", "excused", "unexcused", "elements")}
-    except Exception as e:  # the oracle is test infrastructure; its absence does not stop timing
-        parity = {"error": str(e)}
 
     gelem = elems / (ms * 1e-3) / 1e9
     gbs = elems * BYTES_PER_ELEM / (ms * 1e-3) / 1e9
@@ -475,7 +522,6 @@ def main():
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic() if args.variant == "butterfly" else None},
         "hbm_pct": round(100 * gbs / PEAK_HBM_GBS, 2),
-        "parity": parity,
     }
     if sq_ms is not None:
         sq_gbs = elems * BYTES_PER_ELEM / (sq_ms * 1e-3) / 1e9
@@ -496,6 +542,8 @@ def main():
         out["w4a4_gemm"] = gemm
     if mlp is not None:
         out["mlp_shape"] = mlp
+    if shard is not None:
+        out["shard_8way"] = shard
     if sweep is not None:
         out["sweep_28_calls"] = sweep
     if args.calib_copy_mib > 0:
@@ -506,11 +554,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(x0, p0, args.cpu_seconds)
-        try:
-            out["cpu_oracles"] = cpu_oracles(x0, p0, out["cpu_baseline"]["cores"])
-        except Exception as e:  # the oracle is test infrastructure; its absence does not stop timing
-            out["cpu_oracles"] = {"error": str(e)}
+        kq_step(0)  # set 0 holds the host-generated input
+        torch.cuda.synchronize()
+        out.update(cpu_leg(x0, p0, qs[0].cpu().numpy(), ss[0].cpu().numpy(), args.cpu_seconds))
     print(json.dumps(out), flush=True)
 
 

@@ -142,6 +142,34 @@ def test_ragged_shapes_match_oracle(rows, d):
     assert st["pass"], st
 
 
+def test_eight_way_shards_equal_the_full_call():
+    """One GPU's share at 8-way sharding of the FLUX layer: each token shard X[576,
+    3072] and each channel shard X[4608, 384] with its 12 factor sets gives exactly the
+    matching rows / columns of the full call (every (row, block) unit is independent),
+    and one shard of each kind passes the oracle rule on its own."""
+    cfg = synth.get_config("flux")
+    say("[shards] flux 8 token shards 576x3072, 8 channel shards 4608x384")
+    x, p, _ = synth.make_inputs(cfg)
+    q_full, s_full, _ = run_kq(x, p, debug=False)
+    tr, tc, tb = cfg.rows // 8, cfg.d // 8, cfg.nb // 8
+    for k in range(8):
+        rows = slice(k * tr, (k + 1) * tr)
+        qt, st, _ = run_kq(np.ascontiguousarray(x[rows]), p, debug=False)
+        assert np.array_equal(qt, q_full[rows]) and np.array_equal(st, s_full[rows]), k
+        xc = np.ascontiguousarray(x[:, k * tc:(k + 1) * tc])
+        pc = np.ascontiguousarray(p[k * tb:(k + 1) * tb])
+        qc, sc, _ = run_kq(xc, pc, debug=False)
+        assert np.array_equal(qc, q_full[:, k * tc // 2:(k + 1) * tc // 2]), k
+        assert np.array_equal(sc, s_full[:, k * tb:(k + 1) * tb]), k
+    for xs, ps in [(np.ascontiguousarray(x[3 * tr:4 * tr]), p),
+                   (np.ascontiguousarray(x[:, 5 * tc:6 * tc]), np.ascontiguousarray(p[5 * tb:6 * tb]))]:
+        q, s, y = run_kq(xs, ps)
+        _, _, y_o = oracle.quantize(xs, ps, want_y=True)
+        st = verdict(xs, y_o, q, s, y_c=y)
+        say(f"  {xs.shape}: {st}")
+        assert st["pass"], st
+
+
 def test_row_subsets_and_pitches_with_canaries():
     import torch
     cfg = synth.get_config("sana")

@@ -189,7 +189,8 @@ int hq_transform_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_
  *   rows_per_sample  rows (tokens) per modulation vector, >= 1
  *   eps              >= 0, finite (KQ_ERR_VALUE otherwise)
  *   params           device float32 [d/32][5][3] (KQ_T_PARAMS format)
- * d is at most 16384 here (one row per workgroup; KQ_ERR_SHAPE beyond).
+ * d is at most 16384 here (a row's d/32 blocks, one per lane, must fit in one
+ * workgroup of 512 lanes; KQ_ERR_SHAPE beyond).
  * Computed in fp32: the row mean from a sum reduction, then the variance from the
  * same reduction of the squared deviations (both in a fixed order, so the result
  * is deterministic); the modulation folded into the transform's diagonal plus a

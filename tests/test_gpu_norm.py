@@ -51,7 +51,8 @@ def test_norm_parity(name, rps):
 
 
 @pytest.mark.parametrize("rows,d,rps,eps", [(1, 32, 1, 1e-6), (5, 96, 2, 0.0), (130, 3104, 7, 1e-5),
-                                            (64, 64, 1000, 0.5)])
+                                            (64, 64, 1000, 0.5), (3, 1024, 1, 1e-6),
+                                            (9, 16384, 2, 1e-6), (4, 16352, 3, 1e-6)])
 def test_norm_ragged_and_edge(rows, d, rps, eps):
     say(f"[norm edge] rows={rows} d={d} rps={rps} eps={eps}")
     rng = np.random.default_rng(rows + d)

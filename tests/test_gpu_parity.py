@@ -142,6 +142,20 @@ def test_ragged_shapes_match_oracle(rows, d):
     assert st["pass"], st
 
 
+@pytest.mark.parametrize("rows,nb", [(3, 4096), (2, 4099)])
+def test_wide_rows_match_oracle(rows, nb):
+    """Very wide rows: 4096 blocks, and a prime 4099 blocks (the lane count must be a
+    multiple of nb, so the grid holds far more lanes than units)."""
+    say(f"[wide] rows={rows} nb={nb}")
+    rng = np.random.default_rng(nb)
+    x = synth.bf16_bits_from_f32((rng.normal(size=(rows, 32 * nb)) * 3).astype(np.float32))
+    p = synth.make_params(nb, rng)
+    q, s, y = run_kq(x, p)
+    _, _, y_o = oracle.quantize(x, p, want_y=True)
+    st = verdict(x, y_o, q, s, y_c=y)
+    assert st["pass"], st
+
+
 def test_eight_way_shards_equal_the_full_call():
     """One GPU's share at 8-way sharding of the FLUX layer: each token shard X[576,
     3072] and each channel shard X[4608, 384] with its 12 factor sets gives exactly the

@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true", help="skip the W4A4 product timing")
     ap.add_argument("--no-mlp", action="store_true", help="skip the 4608x12288 quantizer timing")
     ap.add_argument("--no-shard", action="store_true", help="skip the 8-way shard timing")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the timing of independent steps alternating over two streams")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the 28-call batched sweep (14 x 18432x3072 + 14 x 18432x12288)")
     ap.add_argument("--no-norm", action="store_true",
@@ -108,6 +110,44 @@ def timed_graph(fn, steps, warmup):
 
 KERNEL_SOURCES = ("kq_butterfly.hip", "kq_device.hpp", "kq_factors.hpp", "kq_launch.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kq_butterfly_flux_4608x3072_traffic.json")
+
+
+def timed_graph_two_streams(fn, steps, warmup):
+    """As timed_graph, but the captured steps alternate between two streams (even
+    steps on the capture stream, odd ones on a second stream, each chain in order):
+    consecutive steps are independent (distinct buffer sets), so one step's ramp-up
+    may overlap the previous step's drain."""
+    import torch
+    side, other = torch.cuda.Stream(), torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(max(1, warmup)):
+            fn(i)
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()
+            other.wait_stream(cap)
+            for i in range(steps):
+                if i % 2:
+                    with torch.cuda.stream(other):
+                        fn(i)
+                else:
+                    fn(i)
+            cap.wait_stream(other)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        g.replay()
+        side.synchronize()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(side)
+        g.replay()
+        end.record(side)
+        end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
 
 
 def kernel_source_hash() -> str:
@@ -491,6 +531,9 @@ def main():
         sq_ms = None if args.no_sq else timed_graph(sq_step, args.steps, args.warmup)
         hq_ms = None if args.no_sq else timed_graph(hq_step, args.steps, args.warmup)
 
+    # not the headline: independent steps on two streams, so that consecutive calls'
+    # ramp-up and drain may overlap (graph replay only)
+    ov_ms = None if args.no_overlap or args.eager else timed_graph_two_streams(kq_step, args.steps, args.warmup)
     weights = None if args.no_weights else weights_timing(args)
     norm = None if args.no_norm else norm_timing(args, cfg, xs, ps, qs, ss, ms)
     gemm = None if args.no_gemm else gemm_timing(args, qs, ss)
@@ -532,6 +575,12 @@ def main():
                                     "t_hq_over_t_kq": round(hq_ms / ms, 4)}
         out["context"] = ("pages: on an MI350 the KroQuant quantizer kernel ran up to 14% faster "
                           "than a SmoothQuant kernel (shapes and timing method unstated)")
+    if ov_ms is not None:
+        ov_gbs = elems * BYTES_PER_ELEM / (ov_ms * 1e-3) / 1e9
+        out["two_streams"] = {"ms_per_step": round(ov_ms, 6), "gbs": round(ov_gbs, 1),
+                              "hbm_frac": round(ov_gbs / PEAK_HBM_GBS, 4),
+                              "note": "independent steps alternating over two streams in one graph; "
+                                      "not the headline, which times one call after another"}
     if ceiling is not None:
         out["stream_ceiling"] = ceiling
     if weights is not None:

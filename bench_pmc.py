@@ -140,7 +140,7 @@ TRACE_KERNELS = [
 
 def trace(trace_dir, bench_json):
     """Kernel-trace summary (durations per kernel: average, median, p10, p90) of
-    `rocprofv3 --kernel-trace --stats ... -- python3 bench.py --no-cpu --no-sweep --no-shard`, with the
+    `rocprofv3 --kernel-trace --stats ... -- python3 bench.py --no-cpu --no-sweep --no-shard --no-overlap`, with the
     unprofiled bench line of the same build for the cross-check."""
     rows = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0])))
     # bench.py's legs run in order and (without the sweep) the 4608 x 12288 leg comes
@@ -162,8 +162,8 @@ def trace(trace_dir, bench_json):
 
     md = ["# Kernel trace of bench.py, FLUX.1-schnell-like 4608x3072 bf16 workload (one MI355X)", "",
           "Commands (repository root):", "", "```",
-          "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o bench -- python3 bench.py --no-cpu --no-sweep --no-shard",
-          "python3 bench.py --no-cpu --no-sweep --no-shard > out/bench.json",
+          "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o bench -- python3 bench.py --no-cpu --no-sweep --no-shard --no-overlap",
+          "python3 bench.py --no-cpu --no-sweep --no-shard --no-overlap > out/bench.json",
           "python3 bench_pmc.py trace out/trace out/bench.json", "```", "",
           "bench.py replays each timed leg from one captured HIP graph (%d rotating buffer sets for the "
           "4608x3072 legs).  Durations from the trace (end - start per dispatch), microseconds:"

@@ -476,7 +476,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the quantizer needs no cross-GPU exchange; see DESIGN.md for sharding)",
+              "(the quantizer needs no cross-GPU exchange: every (row, block) unit is independent, "
+              "so each GPU quantizes its own shard of rows or of 32-channel blocks)",
               file=sys.stderr)
         sys.exit(2)
     import torch

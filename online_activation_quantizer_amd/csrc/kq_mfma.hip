@@ -49,7 +49,7 @@ constexpr int kChunksPerThread = kTileRows * kChunksPerRow / kThreads;  // 4
 constexpr int kQPitch = kTileBlocks * 16 + 16;    // staged code row: 128 bytes + 16
 static_assert(kTileRows * kTileBlocks * 16 == kThreads * 16, "one 16-byte code store per thread");
 
-constexpr int kMfmaBlocksPerCU = 3;  // resident workgroups per CU (LDS: 33 KB each)
+constexpr int kMfmaBlocksPerCU = 3;  // resident workgroups per CU (LDS: 38 KB each)
 
 // Encodes one block of one token (this lane's half of it): the 16 code bytes go to
 // the workgroup's staging row `qrow` in LDS, the scale byte straight to memory.

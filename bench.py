@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true", help="skip the W4A4 product timing")
     ap.add_argument("--no-mlp", action="store_true", help="skip the 4608x12288 quantizer timing")
     ap.add_argument("--no-shard", action="store_true", help="skip the 8-way shard timing")
+    ap.add_argument("--no-quality", action="store_true",
+                    help="skip the quantization-error comparison of the transforms")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the timing of independent steps alternating over two streams")
     ap.add_argument("--no-sweep", action="store_true",
@@ -283,6 +285,63 @@ def mlp_timing(args):
     return {"workload": f"{cfg.rows}x{cfg.d} bf16, {cfg.nb} factor sets, {args.variant}", "ms_per_call": round(ms, 6),
             "gelem_s": round(elems / (ms * 1e-3) / 1e9, 3), "gbs": round(gbs, 1),
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)  # OCP MX FP4 magnitudes, codes 0..7
+
+
+def mxfp4_values(q, s):
+    """float32 [rows, 32 nb] decoded from MXFP4 codes q [rows, 16 nb] (low nibble first,
+    bit 3 the sign) and E8M0 scales s [rows, nb]; measurement only."""
+    import torch
+    mag = torch.tensor(E2M1_VALUES, dtype=torch.float32, device=q.device)
+    table = torch.cat([mag, -mag])
+    rows = q.shape[0]
+    codes = torch.stack([q & 15, q >> 4], dim=-1).reshape(rows, -1).long()
+    scale = torch.exp2(s.float() - 127.0)
+    return (table[codes].view(rows, -1, 32) * scale.unsqueeze(-1)).view(rows, -1)
+
+
+def quality_leg(x, p_lu, m_dev, times):
+    """Quantization error of the transforms the pages compare, beside their kernel
+    times: relative RMS error ||x_hat - x|| / ||x|| of the activation X (bf16 values)
+    after MXFP4 and the transform's inverse.  For orthogonal transforms (identity,
+    block Hadamard, KroQuant factors that are plane rotations) this is the error of
+    y = T x itself; for the synthetic uncalibrated LU factors x_hat solves
+    T_b x_hat = y_hat per block; for SmoothQuant x_hat = y_hat / mult."""
+    import torch
+
+    import synth
+    import online_activation_quantizer_amd as kq
+    rows, d = x.shape
+    nb = d // 32
+    xf = x.view(torch.bfloat16).double()
+
+    def err(a, b):
+        return round(float(torch.linalg.norm(a.double() - b.double()) / torch.linalg.norm(b.double())), 6)
+
+    out = {"workload": f"{rows}x{d} bf16 (the headline input), relative RMS error after MXFP4"}
+    pid = torch.from_numpy(synth.make_identity_params(nb)).cuda()
+    q, s = kq.kq_quantize(x, pid)
+    out["plain_mxfp4"] = {"rel_err": err(mxfp4_values(q, s), xf), "us_per_call": times.get("kq")}
+    q, s, y = kq.hq_transform_debug(x)
+    out["block_hadamard"] = {"rel_err": err(mxfp4_values(q, s), y), "us_per_call": times.get("hq")}
+    for name, pr in (("kroquant_rotations_45deg", synth.make_rotation_params(nb)),
+                     ("kroquant_random_rotations", synth.make_rotation_params(nb, np.random.default_rng(11)))):
+        q, s, y = kq.kq_transform_debug(x, torch.from_numpy(pr).cuda())
+        out[name] = {"rel_err": err(mxfp4_values(q, s), y), "us_per_call": times.get("kq")}
+    q, s = kq.kq_quantize(x, p_lu)
+    T = kq.kq_expand_factors(p_lu, kq.KQ_T_DENSE_F32).view(nb, 32, 32).double()
+    yh = mxfp4_values(q, s).double().view(rows, nb, 32).permute(1, 2, 0).contiguous()
+    xh = torch.linalg.solve(T, yh).permute(2, 0, 1).reshape(rows, d)
+    out["kroquant_random_lu_factors"] = {"rel_err": err(xh, xf), "us_per_call": times.get("kq"),
+                                         "note": "uncalibrated synthetic factors (ill-conditioned)"}
+    if m_dev is not None:
+        q, s = kq.sq_quantize(x, m_dev)
+        out["smoothquant_random_scales"] = {"rel_err": err(mxfp4_values(q, s).double() / m_dev.double(), xf),
+                                            "us_per_call": times.get("sq")}
+    torch.cuda.synchronize()
+    return out
 
 
 def shard_timing(args, xs, ps):
@@ -541,6 +600,12 @@ def main():
     mlp = None if args.no_mlp else mlp_timing(args)
     shard = None if args.no_shard or args.variant != "butterfly" else shard_timing(args, xs, ps)
     sweep = None if args.no_sweep else sweep_timing(args)
+    quality = None
+    if not args.no_quality:
+        times = {"kq": round(ms * 1e3, 3)}
+        if sq_ms is not None:
+            times.update(sq=round(sq_ms * 1e3, 3), hq=round(hq_ms * 1e3, 3))
+        quality = quality_leg(xs[0], ps[0], m_dev, times)
     ceiling = None if args.no_ceiling else stream_ceiling(args, xs, qs, ss, ms)
 
     gelem = elems / (ms * 1e-3) / 1e9
@@ -594,6 +659,8 @@ def main():
         out["mlp_shape"] = mlp
     if shard is not None:
         out["shard_8way"] = shard
+    if quality is not None:
+        out["quality"] = quality
     if sweep is not None:
         out["sweep_28_calls"] = sweep
     if args.calib_copy_mib > 0:

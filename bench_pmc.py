@@ -3,9 +3,9 @@
 the quantizer kernel, calibrated against a plain copy of known size.
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o fetch -- \\
-        python3 bench.py --steps 8 --warmup 2 --no-cpu --eager --no-gemm --no-ceiling --no-mlp --no-sweep --no-shard --calib-copy-mib 256
+        python3 bench.py --steps 8 --warmup 2 --no-cpu --eager --no-gemm --no-ceiling --no-mlp --no-sweep --no-shard --no-quality --calib-copy-mib 256
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o write -- \\
-        python3 bench.py --steps 8 --warmup 2 --no-cpu --eager --no-gemm --no-ceiling --no-mlp --no-sweep --no-shard --calib-copy-mib 256
+        python3 bench.py --steps 8 --warmup 2 --no-cpu --eager --no-gemm --no-ceiling --no-mlp --no-sweep --no-shard --no-quality --calib-copy-mib 256
     python3 bench_pmc.py DIR 256
 
 FETCH_SIZE / WRITE_SIZE are read in KiB per dispatch.  The copy kernel reads and
@@ -62,9 +62,9 @@ def per_kernel(csv_path, counter):
     return out
 
 
-# (the 4608 x 12288, shard and sweep legs run the same kernel on other shapes: left out)
+# (the 4608 x 12288, shard, quality and sweep legs: left out)
 CMD = ("python3 bench.py --steps 8 --warmup 2 --no-cpu --eager --no-gemm --no-ceiling --no-mlp "
-       "--no-sweep --no-shard --calib-copy-mib %d")
+       "--no-sweep --no-shard --no-quality --calib-copy-mib %d")
 
 
 def main():
@@ -140,7 +140,7 @@ TRACE_KERNELS = [
 
 def trace(trace_dir, bench_json):
     """Kernel-trace summary (durations per kernel: average, median, p10, p90) of
-    `rocprofv3 --kernel-trace --stats ... -- python3 bench.py --no-cpu --no-sweep --no-shard --no-overlap`, with the
+    `rocprofv3 --kernel-trace --stats ... -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap`, with the
     unprofiled bench line of the same build for the cross-check."""
     rows = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0])))
     # bench.py's legs run in order and (without the sweep) the 4608 x 12288 leg comes
@@ -162,8 +162,8 @@ def trace(trace_dir, bench_json):
 
     md = ["# Kernel trace of bench.py, FLUX.1-schnell-like 4608x3072 bf16 workload (one MI355X)", "",
           "Commands (repository root):", "", "```",
-          "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o bench -- python3 bench.py --no-cpu --no-sweep --no-shard --no-overlap",
-          "python3 bench.py --no-cpu --no-sweep --no-shard --no-overlap > out/bench.json",
+          "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o bench -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap",
+          "python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap > out/bench.json",
           "python3 bench_pmc.py trace out/trace out/bench.json", "```", "",
           "bench.py replays each timed leg from one captured HIP graph (%d rotating buffer sets for the "
           "4608x3072 legs).  Durations from the trace (end - start per dispatch), microseconds:"

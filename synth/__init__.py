@@ -10,6 +10,6 @@ from .configs import (  # noqa: F401
 )
 from .gen import (  # noqa: F401
     bf16_bits_from_f32, f32_from_bf16_bits, make_activations, make_activations_device, make_params,
-    make_identity_params,
+    make_identity_params, make_rotation_params,
     make_sq_mult, make_inputs, make_weights, make_modulation,
 )

@@ -63,6 +63,20 @@ def make_identity_params(nb: int) -> np.ndarray:
     return p
 
 
+def make_rotation_params(nb: int, rng: np.random.Generator | None = None,
+                         angle: float = np.pi / 4) -> np.ndarray:
+    """Factor parameters [nb][5][3] (l, u, v) whose factors are plane rotations
+    [[c, s], [-s, c]] (orthogonal, unit determinant): u = c, v = s, l = -s / c.
+    Every factor at `angle`, or (with rng) angles uniform in (-pi/3, pi/3), so c >= 1/2."""
+    th = (np.full((nb, 5), angle) if rng is None else rng.uniform(-np.pi / 3, np.pi / 3, size=(nb, 5)))
+    c, s = np.cos(th), np.sin(th)
+    p = np.empty((nb, 5, 3), np.float32)
+    p[..., 0] = -s / c
+    p[..., 1] = c
+    p[..., 2] = s
+    return p
+
+
 def make_sq_mult(d: int, rng: np.random.Generator) -> np.ndarray:
     s = np.exp(rng.normal(0.0, 0.5, size=d))
     return (1.0 / s).astype(np.float32)

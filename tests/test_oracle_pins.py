@@ -75,6 +75,25 @@ def test_p2_kron_of_inverses_is_inverse(oq):
         assert err <= 1e-12 * max(1.0, np.abs(T[b]).max() * np.abs(Ti[b]).max())
 
 
+def test_rotation_factors_give_an_orthogonal_transform(oq):
+    # L U = [[c, s], [-s, c]] for (l, u, v) = (-s/c, c, s); a Kronecker product of
+    # orthogonal factors is orthogonal, so T_b T_b^T = I and the inverse is T_b^T
+    # (up to the float32 rounding of the parameters)
+    import synth
+    for p in (synth.make_rotation_params(8), synth.make_rotation_params(16, np.random.default_rng(4))):
+        T, Ti = oq.expand(p), oq.expand(p, inverse=True)
+        for b in range(p.shape[0]):
+            assert np.abs(T[b] @ T[b].T - np.eye(32)).max() < 5e-6
+            assert np.abs(Ti[b] - T[b].T).max() < 5e-6
+    c = s = np.sqrt(0.5)
+    F1 = np.array([[c, s], [-s, c]])
+    T = oq.expand(synth.make_rotation_params(1))[0]
+    ref = F1
+    for _ in range(4):
+        ref = np.kron(ref, F1)
+    assert np.abs(T - ref).max() < 1e-6
+
+
 def test_p6_parameter_count_below_half_of_per_channel():
     # abstract: fewer than half the parameters of per-channel scaling.
     per_block = 5 * 3  # five factors, three free parameters (l, u, v) each

@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-shard", action="store_true", help="skip the 8-way shard timing")
     ap.add_argument("--no-quality", action="store_true",
                     help="skip the quantization-error comparison of the transforms")
+    ap.add_argument("--warm-ms", type=float, default=100.0,
+                    help="untimed graph replays before each timed one, at least this many ms")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the timing of independent steps alternating over two streams")
     ap.add_argument("--no-sweep", action="store_true",
@@ -79,11 +81,26 @@ def timed(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps
 
 
+WARM_MS = 100.0  # untimed replays before each timed one: at least this much GPU time
+
+
+def warm_replays(g, stream):
+    """Replays g untimed until WARM_MS of GPU time has passed (at least once), so the
+    timed replay starts from the clocks of sustained work, not from an idle GPU."""
+    t0 = time.perf_counter()
+    while True:
+        g.replay()
+        stream.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= WARM_MS:
+            break
+
+
 def timed_graph(fn, steps, warmup):
     """Average milliseconds per step when exactly `steps` steps (fn(0) .. fn(steps-1))
     are replayed from one captured HIP graph.  The graph holds the same kernel
     launches on the same buffers as the eager loop; it only removes the per-launch
-    host work.  One untimed replay (after `warmup` eager steps) precedes the timed one."""
+    host work.  Untimed replays for at least WARM_MS (after `warmup` eager steps)
+    precede the timed one."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -98,8 +115,7 @@ def timed_graph(fn, steps, warmup):
                 fn(i)
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
-        g.replay()
-        side.synchronize()
+        warm_replays(g, side)
         torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(side)
@@ -140,8 +156,7 @@ def timed_graph_two_streams(fn, steps, warmup):
             cap.wait_stream(other)
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
-        g.replay()
-        side.synchronize()
+        warm_replays(g, side)
         torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(side)
@@ -533,6 +548,8 @@ def cpu_oracles(x0, p0, threads):
 
 def main():
     args = parse()
+    global WARM_MS
+    WARM_MS = args.warm_ms
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the quantizer needs no cross-GPU exchange: every (row, block) unit is independent, "

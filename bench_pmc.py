@@ -57,7 +57,9 @@ def per_kernel(csv_path, counter):
                 out[key].append(v)
                 break
         else:
-            if "copy" in name.lower() and "bfloat16" not in name:
+            # the calibration copy (a device-to-device tensor copy) runs on the runtime's
+            # buffer-copy kernel; torch's elementwise copy kernels are not it
+            if name.startswith("__amd_rocclr_copyBuffer"):
                 out["copy"].append(v)
     return out
 
@@ -140,7 +142,7 @@ TRACE_KERNELS = [
 
 def trace(trace_dir, bench_json):
     """Kernel-trace summary (durations per kernel: average, median, p10, p90) of
-    `rocprofv3 --kernel-trace --stats ... -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap`, with the
+    `rocprofv3 --kernel-trace --stats ... -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap --warm-ms 10`, with the
     unprofiled bench line of the same build for the cross-check."""
     rows = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0])))
     # bench.py's legs run in order and (without the sweep) the 4608 x 12288 leg comes
@@ -162,7 +164,7 @@ def trace(trace_dir, bench_json):
 
     md = ["# Kernel trace of bench.py, FLUX.1-schnell-like 4608x3072 bf16 workload (one MI355X)", "",
           "Commands (repository root):", "", "```",
-          "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o bench -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap",
+          "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o bench -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap --warm-ms 10",
           "python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap > out/bench.json",
           "python3 bench_pmc.py trace out/trace out/bench.json", "```", "",
           "bench.py replays each timed leg from one captured HIP graph (%d rotating buffer sets for the "

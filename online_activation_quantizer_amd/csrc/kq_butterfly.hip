@@ -56,10 +56,6 @@ __global__ __launch_bounds__(kThreads) void butterfly_kernel(
   const uint32_t b = gtid % nb;
   const uint32_t t = gtid / nb;
   if (t >= rows) return;
-  // parameter loads first: the set-up then waits for them only
-  BlockParams bp;
-  if (MODE != kHadamard) bp = load_params(params, b);
-  __builtin_amdgcn_sched_barrier(0);
   BlockConsts c;
   uint8_t* const qcol = q + b * (kBlk / 2);
   uint8_t* const scol = s + b;
@@ -67,7 +63,8 @@ __global__ __launch_bounds__(kThreads) void butterfly_kernel(
   for_each_row<DT, kRowDepth>(
       x + (size_t)b * kBlk * (DT == DT_BF16 ? 2 : 4), rows, ldx, t, tstep,
       [&] {
-        if (MODE != kHadamard) make_consts<MODE == kWeights>(bp, c);
+        // the block's factors, after the first rows' loads (4608 x 3072: 9.03 -> 8.69 us)
+        if (MODE != kHadamard) make_consts<MODE == kWeights>(load_params(params, b), c);
       },
       [&](float (&v)[kBlk], uint32_t r) {
         if (MODE == kHadamard) hadamard(v);

@@ -54,9 +54,9 @@ __device__ __forceinline__ void unpack(const Raw<DT_FP32>& r, float (&v)[kBlk]) 
 // the lane's block column in row 0 and `ldx` is the row pitch in bytes; row
 // arithmetic is 32-bit, so every address is one multiply-add.  The loads run
 // DEPTH rows ahead in a ring of raw buffers.
-//  - The caller issues its own parameter loads before calling, so they are the
-//    oldest memory operations and `setup` (run after the first DEPTH rows are
-//    requested) waits for them only, not for the rows.
+//  - `setup` runs after the first DEPTH rows are requested and loads the lane's
+//    constants there: the rows' DRAM requests leave first, and the constants
+//    (cache hits shared by many lanes) return while those are in flight.
 //  - Each slot is refilled right after it is unpacked, before its row's math and
 //    stores, so a refill is in flight during DEPTH rows of work and the memory
 //    operations of every slot come in the same order (refill, then stores).  The
@@ -74,7 +74,8 @@ __device__ __forceinline__ void for_each_row(const uint8_t* __restrict__ xcol, u
   Raw<DT> ring[DEPTH];
 #pragma unroll
   for (int k = 0; k < DEPTH; ++k) ring[k] = load_raw<DT>(row_ptr(t + k * tstep));
-  // keep the row loads behind the caller's parameter loads and ahead of the set-up
+  // the first rows' loads leave before the set-up, whose loads of the lane's
+  // constants (cache hits) would otherwise queue ahead of them
   __builtin_amdgcn_sched_barrier(0);
   setup();
   __builtin_amdgcn_sched_barrier(0);

@@ -22,14 +22,7 @@ __global__ __launch_bounds__(kThreads) void sq_kernel(
   const uint32_t b = gtid % nb;
   const uint32_t t = gtid / nb;
   if (t >= rows) return;
-  // multiplier loads first: they complete before the rows
-  float4 mr[8];
-  {
-    const float4* mp = reinterpret_cast<const float4*>(mult + (size_t)b * kBlk);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) mr[k] = mp[k];
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  const float4* const mp = reinterpret_cast<const float4*>(mult + (size_t)b * kBlk);
   float m[kBlk];
   uint8_t* const qcol = q + b * (kBlk / 2);
   uint8_t* const scol = s + b;
@@ -37,12 +30,14 @@ __global__ __launch_bounds__(kThreads) void sq_kernel(
   for_each_row<DT, kRowDepth>(
       x + (size_t)b * kBlk * (DT == DT_BF16 ? 2 : 4), rows, ldx, t, tstep,
       [&] {
+        // the block's multipliers, after the first rows' loads
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          m[4 * k] = mr[k].x;
-          m[4 * k + 1] = mr[k].y;
-          m[4 * k + 2] = mr[k].z;
-          m[4 * k + 3] = mr[k].w;
+          const float4 mr = mp[k];
+          m[4 * k] = mr.x;
+          m[4 * k + 1] = mr.y;
+          m[4 * k + 2] = mr.z;
+          m[4 * k + 3] = mr.w;
         }
       },
       [&](float (&v)[kBlk], uint32_t r) {

@@ -127,7 +127,7 @@ TRACE_KERNELS = [
      "`butterfly_kernel<bf16, -, forward>` (kq_quantize; also the quantize step of the unfused sequence)"),
     ("void kq::(anonymous namespace)::butterfly_kernel<0, false, 2>", "`butterfly_kernel<bf16, -, hadamard>` (hq_quantize)"),
     ("void kq::(anonymous namespace)::sq_kernel<0, false>", "`sq_kernel<bf16>` (sq_quantize)"),
-    ("(anonymous namespace)::stream_kernel", "`stream_kernel` (same-bytes ceiling, 5 grid sizes)"),
+    ("(anonymous namespace)::stream_kernel", "`stream_kernel` (same-bytes ceiling, 5 grid sizes; when traced)"),
     ("void kq::(anonymous namespace)::norm_kernel<0, true, false>", "`norm_kernel<bf16, modulated>` (kq_norm_quantize)"),
     ("void kq::(anonymous namespace)::butterfly_kernel<0, false, 1>",
      "`butterfly_kernel<bf16, -, weights>` (kq_quantize_weights, 12288x3072)"),
@@ -142,7 +142,7 @@ TRACE_KERNELS = [
 
 def trace(trace_dir, bench_json):
     """Kernel-trace summary (durations per kernel: average, median, p10, p90) of
-    `rocprofv3 --kernel-trace --stats ... -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap --warm-ms 10`, with the
+    `rocprofv3 --kernel-trace --stats ... -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap --no-ceiling`, with the
     unprofiled bench line of the same build for the cross-check."""
     rows = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0])))
     # bench.py's legs run in order and (without the sweep) the 4608 x 12288 leg comes
@@ -164,7 +164,7 @@ def trace(trace_dir, bench_json):
 
     md = ["# Kernel trace of bench.py, FLUX.1-schnell-like 4608x3072 bf16 workload (one MI355X)", "",
           "Commands (repository root):", "", "```",
-          "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o bench -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap --warm-ms 10",
+          "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o bench -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap --no-ceiling",
           "python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap > out/bench.json",
           "python3 bench_pmc.py trace out/trace out/bench.json", "```", "",
           "bench.py replays each timed leg from one captured HIP graph (%d rotating buffer sets for the "

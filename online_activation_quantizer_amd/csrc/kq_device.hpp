@@ -56,7 +56,9 @@ __device__ __forceinline__ void unpack(const Raw<DT_FP32>& r, float (&v)[kBlk]) 
 // DEPTH rows ahead in a ring of raw buffers.
 //  - `setup` runs after the first DEPTH rows are requested and loads the lane's
 //    constants there: the rows' DRAM requests leave first, and the constants
-//    (cache hits shared by many lanes) return while those are in flight.
+//    (cache hits shared by many lanes) return while those are in flight.  Every
+//    lane runs it, also one whose first row t is past the end (its loads are
+//    clamped in bounds), so a set-up may hold a workgroup barrier.
 //  - Each slot is refilled right after it is unpacked, before its row's math and
 //    stores, so a refill is in flight during DEPTH rows of work and the memory
 //    operations of every slot come in the same order (refill, then stores).  The
@@ -79,6 +81,9 @@ __device__ __forceinline__ void for_each_row(const uint8_t* __restrict__ xcol, u
   __builtin_amdgcn_sched_barrier(0);
   setup();
   __builtin_amdgcn_sched_barrier(0);
+  // lanes with no row (past the last unit) run the set-up with the others, since it
+  // may hold a workgroup barrier, and stop here
+  if (t > last) return;
   // one round over the ring; false once the rows are done
   auto round = [&]() -> bool {
 #pragma unroll

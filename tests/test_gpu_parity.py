@@ -47,6 +47,21 @@ def test_sq_parity(name):
     assert st["pass"], st
 
 
+@pytest.mark.parametrize("rows,nb", [(1, 1), (33, 97), (5, 300), (257, 3)])
+def test_sq_ragged_and_wide(rows, nb):
+    """SmoothQuant on shapes whose grid has lanes past the last row (they join the
+    workgroup's multiplier staging and stop) and on more blocks than a workgroup's
+    lanes (300: each workgroup stages the slice its lanes cover)."""
+    say(f"[sq ragged] rows={rows} nb={nb}")
+    rng = np.random.default_rng(rows * 31 + nb)
+    x = synth.bf16_bits_from_f32((rng.normal(size=(rows, 32 * nb)) * 3).astype(np.float32))
+    m = synth.make_sq_mult(32 * nb, rng)
+    q, s = kq.sq_quantize(dev(x), dev(m))
+    _, _, y_o = oracle.sq_quantize(x, m, want_y=True)
+    st = verdict(x, y_o, host(q), host(s))
+    assert st["pass"], st
+
+
 def test_identity_factors_are_plain_mxfp4_exactly():
     cfg = synth.get_config("pixart")
     say("[identity] pixart")

@@ -30,7 +30,7 @@ def test_kq_parity_full_config(name):
     assert st["pass"], st
 
 
-@pytest.mark.parametrize("name", ["pixart", "flux"])
+@pytest.mark.parametrize("name", ["tiny", "pixart", "flux"])
 def test_sq_parity(name):
     cfg = synth.get_config(name)
     say(f"[sq parity] {name}")

@@ -465,10 +465,19 @@ hipError_t launch_mx_gemm(const GemmArgs& g) {
   using T = ProductTiling;
   const int64_t tiles_m = (g.M + T::kBM - 1) / T::kBM, tiles_n = (g.N + T::kBN - 1) / T::kBN;
   const int64_t ntiles = tiles_m * tiles_n;
-  // persistent: one workgroup per compute unit (its LDS holds one), rounded down to
-  // a multiple of 8 so that a workgroup's tiles all fall to its XCD's share
+  // persistent: at most one workgroup per compute unit (its LDS holds one), a
+  // multiple of 8 so that a workgroup's tiles all fall to its XCD's share; and no
+  // more workgroups than keep the number of tile rounds, so every workgroup runs
+  // the same number of tiles up to one (4608 x 12288: 864 tiles, 216 workgroups of
+  // 4 instead of 256 of 3 or 4: 121.9 -> 120.1 us)
   int64_t grid = g.cus >= 8 ? g.cus / 8 * 8 : 8;
   if (grid > ntiles) grid = ntiles;
+  {
+    const int64_t rounds = (ntiles + grid - 1) / grid;
+    int64_t even = (ntiles + rounds - 1) / rounds;
+    even = (even + 7) / 8 * 8;
+    if (even < grid) grid = even;
+  }
   const int64_t xcd_cols = tiles_n % 8 == 0 && grid % 8 == 0 ? tiles_n / 8 : 0;
   // whole 32-bit scale words when every scale row starts 4-byte aligned and holds one
   const bool words = ((uintptr_t)g.sa % 4 == 0) && ((uintptr_t)g.sb % 4 == 0) && g.ldsa % 4 == 0 &&

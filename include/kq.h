@@ -118,7 +118,7 @@ int kq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
 /* SmoothQuant baseline on the same memory skeleton: y[t][c] = x[t][c] * mult[c]
  * (mult = 1/s_c in float32, the per-channel smoothing the abstract compares
  * against), then the same MXFP4 encoding and layout as kq_quantize.
- *   mult    device float32 [d]
+ *   mult    device float32 [d], 16-byte aligned (KQ_ERR_ALIGN otherwise)
  * Errors: as kq_quantize (KQ_ERR_FORMAT and KQ_ERR_VARIANT never occur). */
 int sq_quantize(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx,
                 const float* mult, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,

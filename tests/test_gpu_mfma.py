@@ -55,6 +55,31 @@ def test_mfma_ragged(rows, d):
     assert st["pass"], st
 
 
+def test_mfma_pitched_with_canaries():
+    """Padded pitches on x, q and s: the padding of x holds huge values that must never
+    be read, and the bytes past d/2 and d/32 in q and s must stay untouched; the
+    result equals the unpitched call byte for byte.  97 blocks leave a last group of
+    one block, 77 rows a partial last tile."""
+    import torch
+    rows, d = 77, 3104
+    say(f"[mfma pitch] rows={rows} d={d}")
+    rng = np.random.default_rng(97)
+    x = synth.bf16_bits_from_f32(rng.normal(size=(rows, d)).astype(np.float32) * 4)
+    p = synth.make_params(d // 32, rng)
+    q0, s0, _ = run_kq(x, p, debug=False, variant=kq.KQ_MFMA)
+    xw = np.zeros((rows, d + 64), np.uint16)
+    xw[:, :d] = x
+    xw[:, d:] = synth.bf16_bits_from_f32(np.full((rows, 64), 3e38, np.float32))
+    t = kq.kq_expand_factors(dev(p), kq.KQ_T_DENSE_BF16X3)
+    qbuf = torch.full((rows, d // 2 + 48), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((rows, d // 32 + 9), 0x5A, dtype=torch.uint8, device="cuda")
+    kq.kq_quantize(dev(xw)[:, :d], t, kq.KQ_T_DENSE_BF16X3, kq.KQ_MFMA, q=qbuf[:, : d // 2], s=sbuf[:, : d // 32])
+    torch.cuda.synchronize()
+    qb, sb = qbuf.cpu().numpy(), sbuf.cpu().numpy()
+    assert np.array_equal(qb[:, : d // 2], q0) and np.array_equal(sb[:, : d // 32], s0)
+    assert np.all(qb[:, d // 2:] == 0xA5) and np.all(sb[:, d // 32:] == 0x5A)
+
+
 def test_mfma_rejects_fp32_input():
     x = np.zeros((4, 64), np.float32)
     p = synth.make_identity_params(2)

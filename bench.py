@@ -455,9 +455,43 @@ def gemm_timing(args, qs, ss):
     ms = (timed(step, steps, args.warmup, torch.cuda.current_stream()) if args.eager
           else timed_graph(step, steps, min(args.warmup, 10)))
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-    return {"workload": f"FLUX.1-schnell MLP up-projection {M}x{N}x{K}, fp4 x fp4 (MXFP4), bf16 out",
-            "ms_per_call": round(ms, 6), "tflops": round(tflops, 1),
-            "mfma_frac_fp4": round(tflops / PEAK_FP4_TFLOPS, 4)}
+    res = {"workload": f"FLUX.1-schnell MLP up-projection {M}x{N}x{K}, fp4 x fp4 (MXFP4), bf16 out",
+           "ms_per_call": round(ms, 6), "tflops": round(tflops, 1),
+           "mfma_frac_fp4": round(tflops / PEAK_FP4_TFLOPS, 4)}
+    if not args.eager:
+        res["library_baseline"] = library_gemm_timing(args, qs, ss, qw, sw, out)
+    return res
+
+
+def library_gemm_timing(args, qs, ss, qw, sw, ours):
+    """The same MXFP4 x MXFP4 product through torch's scaled matmul (the vendor BLAS
+    path; block-scaled products come out in bf16 only), timed the same way, with its
+    relative difference to kq_mx_gemm's bf16 output (one bf16 unit in the last place
+    on about half of the elements: the two round the fp32 sums differently);
+    context only."""
+    import torch
+    try:
+        wq, ws = qw.view(torch.float4_e2m1fn_x2).t(), sw.view(torch.float8_e8m0fnu).flatten()
+        P = len(qs)
+        aq = [q.view(torch.float4_e2m1fn_x2) for q in qs]
+        as_ = [s.view(torch.float8_e8m0fnu).flatten() for s in ss]
+        # `ours` holds the output of the graph's last step, on this set
+        j_last = (max(8, args.steps // 10) - 1) % P
+        lib_last = torch._scaled_mm(aq[j_last], wq, as_[j_last], ws, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        rel = float((lib_last.float() - ours.float()).norm() / ours.float().norm())
+
+        def step(i):
+            j = i % P
+            torch._scaled_mm(aq[j], wq, as_[j], ws, out_dtype=torch.bfloat16)
+
+        ms = timed_graph(step, max(8, args.steps // 10), min(args.warmup, 10))
+        M, N, K = qs[0].shape[0], qw.shape[0], qs[0].shape[1] * 2
+        return {"how": "torch._scaled_mm, float4_e2m1fn_x2 operands, float8_e8m0fnu block scales",
+                "ms_per_call": round(ms, 6), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1),
+                "rel_diff_vs_kq_mx_gemm": round(rel, 5)}
+    except Exception as e:  # not every torch build has the fp4 scaled matmul
+        return {"unavailable": f"{type(e).__name__}: {str(e)[:200]}"}
 
 
 def weights_timing(args):

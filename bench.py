@@ -65,20 +65,42 @@ def parse():
     return ap.parse_args()
 
 
+REPLAYS = 7  # timed repetitions of each leg; the line reports their median (p10 and p90 beside it)
+
+
+class Timing(float):
+    """Milliseconds per step: the median over the timed repetitions of a leg, with
+    the 10th and 90th percentiles and the repetition count as attributes."""
+
+    def __new__(cls, samples):
+        a = np.asarray(samples, np.float64)
+        t = super().__new__(cls, float(np.median(a)))
+        t.p10, t.p90, t.n = float(np.percentile(a, 10)), float(np.percentile(a, 90)), len(a)
+        return t
+
+    def summary(self, steps):
+        return {"replays": self.n, "steps_per_replay": steps, "median_ms": round(float(self), 6),
+                "p10_ms": round(self.p10, 6), "p90_ms": round(self.p90, 6)}
+
+
 def timed(fn, steps, warmup, stream):
-    """Average milliseconds per call of fn(i) over `steps` calls, HIP events on `stream`."""
+    """Milliseconds per call of fn(i): REPLAYS repetitions of `steps` calls launched
+    from Python, each timed with HIP events on `stream`."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        fn(i)
-    end.record(stream)
-    end.synchronize()
+    samples = []
+    for _ in range(REPLAYS):
+        start.record(stream)
+        for i in range(steps):
+            fn(i)
+        end.record(stream)
+        end.synchronize()
+        samples.append(start.elapsed_time(end) / steps)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    return Timing(samples)
 
 
 WARM_MS = 100.0  # untimed replays before each timed one: at least this much GPU time
@@ -95,12 +117,29 @@ def warm_replays(g, stream):
             break
 
 
+def _replay_timed(g, stream):
+    """REPLAYS timed replays of graph g on `stream` (after the untimed warm-up
+    replays); milliseconds per replay."""
+    import torch
+    warm_replays(g, stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = []
+    for _ in range(REPLAYS):
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        end.synchronize()
+        out.append(start.elapsed_time(end))
+    return out
+
+
 def timed_graph(fn, steps, warmup):
-    """Average milliseconds per step when exactly `steps` steps (fn(0) .. fn(steps-1))
-    are replayed from one captured HIP graph.  The graph holds the same kernel
-    launches on the same buffers as the eager loop; it only removes the per-launch
-    host work.  Untimed replays for at least WARM_MS (after `warmup` eager steps)
-    precede the timed one."""
+    """Milliseconds per step when exactly `steps` steps (fn(0) .. fn(steps-1)) are
+    replayed from one captured HIP graph: the median over REPLAYS timed replays.
+    The graph holds the same kernel launches on the same buffers as the eager loop;
+    it only removes the per-launch host work.  Untimed replays for at least WARM_MS
+    (after `warmup` eager steps) precede the timed ones."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -115,15 +154,9 @@ def timed_graph(fn, steps, warmup):
                 fn(i)
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
-        warm_replays(g, side)
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(side)
-        g.replay()
-        end.record(side)
-        end.synchronize()
+        samples = _replay_timed(g, side)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    return Timing([t / steps for t in samples])
 
 
 KERNEL_SOURCES = ("kq_butterfly.hip", "kq_device.hpp", "kq_factors.hpp", "kq_launch.hpp")
@@ -156,15 +189,9 @@ def timed_graph_two_streams(fn, steps, warmup):
             cap.wait_stream(other)
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
-        warm_replays(g, side)
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(side)
-        g.replay()
-        end.record(side)
-        end.synchronize()
+        samples = _replay_timed(g, side)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    return Timing([t / steps for t in samples])
 
 
 def kernel_source_hash() -> str:
@@ -206,26 +233,63 @@ def cpu_baseline(x, p, seconds):
                       f"({el:.1f} s, fp64 dense 32x32 per block + MXFP4 encode)"}
 
 
+CEILING_DESIGNS = (("lane", (768, 1024, 1536, 2048)), ("pair", (512, 768, 864)), ("ring", (256, 768)))
+
+
 def stream_ceiling(args, xs, qs, ss, kq_ms):
-    """The same bytes per call (64 B read, 17 B written per 32-element unit) moved by
-    a kernel with no arithmetic, timed like the quantizer step over the same buffer
-    pool at a few grid sizes; the fastest is the practical ceiling at this size."""
-    from online_activation_quantizer_amd import bench_stream
+    """The same bytes per call (64 B read, 17 B written per 32-element unit) moved
+    with no arithmetic, timed like the quantizer step over the same buffer pool:
+    three access designs at a few grid sizes each (the fastest is the practical
+    ceiling of one call at this size), the read half and the write half alone, and
+    the runtime's device-to-device copy of the same total bytes (half read, half
+    written)."""
+    import torch
+
+    from online_activation_quantizer_amd import bench_stream as bs
     P = len(xs)
-    best = None
-    for grid in (768, 1024, 1536, 2048, 3072):
-        def step(i, grid=grid):
-            j = i % P
-            bench_stream.kq_bench_stream(xs[j], qs[j], ss[j], grid)
-        ms = (timed(step, args.steps, args.warmup, __import__("torch").cuda.current_stream())
-              if args.eager else timed_graph(step, args.steps, args.warmup))
-        if best is None or ms < best[0]:
-            best = (ms, grid)
-    ms, grid = best
     elems = xs[0].numel()
+    units = elems // 32
+    run = (lambda f: timed(f, args.steps, args.warmup, torch.cuda.current_stream())) if args.eager else \
+        (lambda f: timed_graph(f, args.steps, args.warmup))
+
+    def leg(design, grid):
+        def step(i):
+            j = i % P
+            bs.kq_bench_stream(xs[j], qs[j], ss[j], grid, design=design)
+        return run(step)
+
+    designs, best = {}, None
+    codes = {"lane": bs.KQB_LANE, "pair": bs.KQB_PAIR, "ring": bs.KQB_RING}
+    for name, grids in CEILING_DESIGNS:
+        for grid in grids:
+            ms = leg(codes[name], grid)
+            if name not in designs or ms < designs[name][0]:
+                designs[name] = (ms, grid)
+            if best is None or ms < best[0]:
+                best = (ms, grid, name)
+    ms, grid, name = best
     gbs = elems * BYTES_PER_ELEM / (ms * 1e-3) / 1e9
-    return {"ms_per_step": round(ms, 6), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-            "grid": grid, "kq_time_over_ceiling_time": round(kq_ms / ms, 4)}
+    out = {"ms_per_step": round(ms, 6), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+           "design": name, "grid": grid, "timing": ms.summary(args.steps),
+           "kq_time_over_ceiling_time": round(kq_ms / ms, 4),
+           "designs": {k: {"us": round(v[0] * 1e3, 3), "grid": v[1]} for k, v in designs.items()}}
+    for key, design, nbytes in (("read_only", bs.KQB_READ, units * 64), ("write_only", bs.KQB_WRITE, units * 17)):
+        t = min(leg(design, g) for g in (1728, 2048))
+        out[key] = {"us": round(t * 1e3, 3), "bytes": nbytes,
+                    "hbm_frac": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    half = (units * 81 // 2) // 256 * 256
+    srcs = [x.view(torch.uint8).view(-1)[:half] for x in xs]
+    dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(P)]
+
+    def copy_step(i):
+        j = i % P
+        dsts[j].copy_(srcs[j])
+    t = run(copy_step)
+    out["runtime_copy"] = {"us": round(t * 1e3, 3), "bytes_moved": 2 * half,
+                           "hbm_frac": round(2 * half / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           "how": "torch copy_ of half the bytes between two device buffers"}
+    del dsts
+    return out
 
 
 def norm_timing(args, cfg, xs, ps, qs, ss, kq_ms):
@@ -563,8 +627,9 @@ def cpu_oracles(x0, p0, threads):
     xs = np.ascontiguousarray(x0[:rows])
     d = x0.shape[1]
     out = {"threads": threads}
-    out["kq_quantize_1_thread_gelem_s"] = round(
-        rate(lambda: oracle.quantize(np.ascontiguousarray(x0[:64]), p0, nthreads=1), 64 * d) / 1e9, 5)
+    one = sorted(rate(lambda: oracle.quantize(x0, p0, nthreads=1), x0.size) for _ in range(3))
+    out["kq_quantize_1_thread_gelem_s"] = round(one[1] / 1e9, 5)
+    out["kq_quantize_1_thread_sample"] = f"the full {x0.shape[0]}x{d} input, median of 3 passes"
     out["hq_quantize_gelem_s"] = round(rate(lambda: oracle.hadamard_quantize(xs, nthreads=threads), rows * d) / 1e9, 5)
     shift, scale = synth.make_modulation(1, d, np.random.default_rng(7))
     out["kq_norm_quantize_gelem_s"] = round(rate(
@@ -669,6 +734,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
+        "timing": ms.summary(args.steps) if isinstance(ms, Timing) else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -686,10 +752,10 @@ def main():
     if sq_ms is not None:
         sq_gbs = elems * BYTES_PER_ELEM / (sq_ms * 1e-3) / 1e9
         out["sq_baseline"] = {"ms_per_step": round(sq_ms, 6), "gbs": round(sq_gbs, 1),
-                              "t_sq_over_t_kq": round(sq_ms / ms, 4)}
+                              "t_sq_over_t_kq": round(sq_ms / ms, 4), "timing": sq_ms.summary(args.steps)}
         hq_gbs = elems * BYTES_PER_ELEM / (hq_ms * 1e-3) / 1e9
         out["hadamard_baseline"] = {"ms_per_step": round(hq_ms, 6), "gbs": round(hq_gbs, 1),
-                                    "t_hq_over_t_kq": round(hq_ms / ms, 4)}
+                                    "t_hq_over_t_kq": round(hq_ms / ms, 4), "timing": hq_ms.summary(args.steps)}
         out["context"] = ("pages: on an MI350 the KroQuant quantizer kernel ran up to 14% faster "
                           "than a SmoothQuant kernel (shapes and timing method unstated)")
     if ov_ms is not None:

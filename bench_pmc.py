@@ -105,9 +105,9 @@ def main():
     json.dump(res, open(bench.TRAFFIC_FILE, "w"), indent=1)
     md = ["# HBM traffic of the quantizer kernels (FETCH_SIZE / WRITE_SIZE), one MI355X", "",
           "Commands (repository root):", "", "```",
-          "rocprofv3 --pmc FETCH_SIZE --output-format csv -d out/pmc/fetch -o fetch -- " + CMD % mib,
-          "rocprofv3 --pmc WRITE_SIZE --output-format csv -d out/pmc/write -o write -- " + CMD % mib,
-          "python3 bench_pmc.py out/pmc %d" % mib, "```", "",
+          "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch -o fetch -- " + CMD % mib,
+          "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write -o write -- " + CMD % mib,
+          "python3 bench_pmc.py gpurun_out/pmc %d" % mib, "```", "",
           "Counters are medians per dispatch, scaled by what the same counter reads for a plain "
           "%d MiB device copy (read scale %.4f, write scale %.4f)." % (mib, f_scale, w_scale), "",
           "| kernel | read bytes / launch | algorithmic read | write bytes / launch | algorithmic write | total / algorithmic |",
@@ -164,9 +164,9 @@ def trace(trace_dir, bench_json):
 
     md = ["# Kernel trace of bench.py, FLUX.1-schnell-like 4608x3072 bf16 workload (one MI355X)", "",
           "Commands (repository root):", "", "```",
-          "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o bench -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap --no-ceiling",
-          "python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap > out/bench.json",
-          "python3 bench_pmc.py trace out/trace out/bench.json", "```", "",
+          "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o bench -- python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap --no-ceiling",
+          "python3 bench.py --no-cpu --no-sweep --no-shard --no-quality --no-overlap > gpurun_out/bench.json",
+          "python3 bench_pmc.py trace gpurun_out/trace gpurun_out/bench.json", "```", "",
           "bench.py replays each timed leg from one captured HIP graph (%d rotating buffer sets for the "
           "4608x3072 legs).  Durations from the trace (end - start per dispatch), microseconds:"
           % b.get("config", {}).get("pool_sets", 0), "",
@@ -190,8 +190,70 @@ def trace(trace_dir, bench_json):
     print("\n".join(md))
 
 
+CLOCK_KERNELS = [
+    ("void kq::(anonymous namespace)::butterfly_kernel<0, false, 0>", "kq_quantize (butterfly)"),
+    ("void kq::(anonymous namespace)::butterfly_kernel<0, false, 2>", "hq_quantize (block Hadamard)"),
+    ("void kq::(anonymous namespace)::sq_kernel<0, false>", "sq_quantize (SmoothQuant)"),
+    ("(anonymous namespace)::stream_kernel", "same bytes, one unit per lane"),
+    ("(anonymous namespace)::stream_pair_kernel", "same bytes, two units per lane"),
+    ("(anonymous namespace)::stream_ring_kernel", "same bytes, two units in flight"),
+    ("(anonymous namespace)::stream_read_kernel", "read half alone"),
+    ("(anonymous namespace)::stream_write_kernel", "write half alone"),
+]
+CLOCK_CMD = ("python3 bench.py --steps 20 --warmup 5 --no-cpu --eager --no-weights --no-norm --no-gemm --no-mlp "
+             "--no-shard --no-quality --no-sweep --no-overlap")
+CLOCK_COUNTERS = "GRBM_GUI_ACTIVE GRBM_COUNT SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY"
+
+
+def clock(run_dir):
+    """Per-kernel medians of a `rocprofv3 --kernel-trace --pmc CLOCK_COUNTERS` run of
+    CLOCK_CMD: duration, the counters, and the clock they imply (GRBM_GUI_ACTIVE
+    cycles of the busy GPU over the dispatch's duration)."""
+    ctr = list(csv.DictReader(open(glob.glob(os.path.join(run_dir, "*counter_collection.csv"))[0])))
+    kt = glob.glob(os.path.join(run_dir, "*kernel_trace.csv"))
+    times = {}
+    if kt:
+        for r in csv.DictReader(open(kt[0])):
+            times[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+    per = {}
+    for r in ctr:
+        key = next((k for k, _ in CLOCK_KERNELS if r["Kernel_Name"].startswith(k)), None)
+        if key is None:
+            continue
+        d = per.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if "Start_Timestamp" in r and r.get("End_Timestamp"):
+            d["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        elif r["Dispatch_Id"] in times:
+            d["_us"] = times[r["Dispatch_Id"]]
+    names = CLOCK_COUNTERS.split()
+    md = ["# Clock and instruction counters per kernel, 4608x3072 bf16 (one MI355X)", "",
+          "Commands (repository root):", "", "```",
+          "rocprofv3 --kernel-trace --pmc " + CLOCK_COUNTERS + " --output-format csv -d gpurun_out/clock -o clock -- "
+          + CLOCK_CMD, "python3 bench_pmc.py clock gpurun_out/clock", "```", "",
+          "Medians per dispatch (counters summed over the device).  `MHz` = GRBM_GUI_ACTIVE / duration; "
+          "`VALU/wave` = SQ_INSTS_VALU / SQ_WAVES.", "",
+          "| kernel | dispatches | us | " + " | ".join(names) + " | MHz | VALU/wave |",
+          "|---|---|---|" + "---|" * len(names) + "---|---|"]
+    for key, label in CLOCK_KERNELS:
+        ds = [d for d in per.get(key, {}).values() if "_us" in d]
+        if not ds:
+            continue
+        med = {n: statistics.median(d.get(n, 0.0) for d in ds) for n in names}
+        us = statistics.median(d["_us"] for d in ds)
+        mhz = med["GRBM_GUI_ACTIVE"] / us if us else 0.0
+        vpw = med["SQ_INSTS_VALU"] / med["SQ_WAVES"] if med["SQ_WAVES"] else 0.0
+        md.append(f"| {label} | {len(ds)} | {us:.2f} | " + " | ".join(f"{med[n]:,.0f}" for n in names)
+                  + f" | {mhz:,.0f} | {vpw:.0f} |")
+    md.append("")
+    open(os.path.join(ROOT, "profiles", "kq_kernels_flux_4608x3072_clock.md"), "w").write("\n".join(md))
+    print("\n".join(md))
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(sys.argv[2], sys.argv[3])
+    elif sys.argv[1] == "clock":
+        clock(sys.argv[2])
     else:
         main()

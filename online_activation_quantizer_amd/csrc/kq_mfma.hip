@@ -1,5 +1,6 @@
-// kq_mfma.hip — matrix-core variant: the block transform as small GEMMs
-// (KroQuant abstract: the block-local structure runs as small tensor-core GEMMs).
+// kq_mfma.hip — matrix-core variant: each block's transform as a small matrix
+// product on the matrix cores (KroQuant abstract: the per-block transforms map
+// onto small matrix-unit products).
 //
 // For a 32-channel block b and 32 token rows, Y_b^T (32 channels x 32 tokens) =
 // T_b (32x32) * X_b^T (32 x 32 tokens) on v_mfma_f32_32x32x16_bf16 with fp32

@@ -44,9 +44,14 @@ def test_bench_helper_library(L):
     from online_activation_quantizer_amd import bench_stream
     B = bench_stream.lib()
     names = header_functions("kq_bench.h")
-    assert names == ["kq_bench_stream"]
+    assert names == ["kq_bench_stream", "kq_bench_stream_design"]
     for n in names:
         assert hasattr(B, n), n
+    assert B.kq_bench_stream_design(X, 4, Q, S, 8, 5, None) == SHAPE
+    assert B.kq_bench_stream_design(X, 4, Q, S, 8, -1, None) == SHAPE
+    assert B.kq_bench_stream_design(X, 1 << 30, Q, S, 8, 0, None) == SHAPE
+    assert B.kq_bench_stream_design(None, 4, Q, S, 8, 2, None) == NULL
+    assert B.kq_bench_stream_design(X, 4, Q + 8, S, 8, 1, None) == ALIGN
     assert B.kq_bench_stream(X, 4, Q, S, 0, None) == SHAPE
     assert B.kq_bench_stream(X, -1, Q, S, 8, None) == SHAPE
     assert B.kq_bench_stream(None, 4, Q, S, 8, None) == NULL

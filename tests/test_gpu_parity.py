@@ -102,24 +102,43 @@ def test_encoder_black_box_every_fp32_in_range():
     assert bad == 0, f"{bad} code bytes differ"
 
 
+def _nibbles(q: np.ndarray) -> np.ndarray:
+    return np.stack([q & 15, q >> 4], axis=-1).reshape(q.shape[0], -1)
+
+
 @pytest.mark.parametrize("k", [-149, -140, -127, -126, -110, -100, -30, 0, 30, 100, 115, 125])
 def test_extreme_scales(k):
     """Blocks scaled by 2^k (fp32 input): scale bytes from 0 to 252.  Identity factors
-    (no rounding in the transform) must match exactly at every k, subnormal inputs
-    included.  Random factors run where fp32 arithmetic keeps its relative precision
-    (|x| above the subnormal range, so the 1e-5 * max|x| rule is attainable) and
-    below 2^116 (so |T_b x| < 2^128)."""
+    (no rounding in the transform) must match the oracle at every k, subnormal and
+    signed-zero inputs included: scales bit for bit, codes bit for bit except the
+    sign of a zero code on a +-0 input.  (The oracle's sums start from +0, so a -0.0
+    input gives y = +0 there; the shears keep -0 where every partner is negative or
+    -0.  A zero y sits on the code boundary at 0, so the parity rule excuses either
+    sign, and this test asserts that those are the only excused cases.)  Random
+    factors run where fp32 arithmetic keeps its relative precision (|x| above the
+    subnormal range, so the 1e-5 * max|x| rule is attainable) and below 2^116 (so
+    |T_b x| < 2^128)."""
     say(f"[extreme scale] 2^{k}")
     rng = np.random.default_rng(1000 + k)
     x = (rng.normal(size=(64, 256)) * 2.0 ** k).astype(np.float32)
-    # draws that underflow to -0.0 become +0.0: the transform's sums give +0 for
-    # an exact zero, so -0.0 inputs sit outside the exact identity reduction
-    x[x == 0] = 0.0
+    zeros = x == 0
+    say(f"[extreme scale] 2^{k}: {int(np.count_nonzero(zeros & np.signbit(x)))} inputs -0.0, "
+        f"{int(np.count_nonzero(zeros & ~np.signbit(x)))} +0.0")
     p = synth.make_identity_params(8)
     q, s, y = run_kq(x, p)
-    q_o, s_o, _ = oracle.quantize(x, p)
-    assert np.array_equal(y.view(np.uint32), x.view(np.uint32))
-    assert np.array_equal(s, s_o) and np.array_equal(q, q_o)
+    q_o, s_o, y_o = oracle.quantize(x, p, want_y=True)
+    assert np.array_equal(y[~zeros].view(np.uint32), x[~zeros].view(np.uint32))
+    assert np.all(y[zeros] == 0)
+    assert np.array_equal(s, s_o)
+    n_g, n_o = _nibbles(q), _nibbles(q_o)
+    diff = n_g != n_o
+    assert np.all((n_g ^ n_o)[diff] == 8), "a code differs in more than the sign bit"
+    assert np.all(zeros[diff]), "a sign differs on a nonzero input"
+    st = oracle.classify(x, y_o, q, s, 0, 1e-5, y_c=y)
+    assert st["unexcused"] == 0 and st["prequant_violations"] == 0, st
+    assert st["excused"] == np.count_nonzero(diff), (st, int(np.count_nonzero(diff)))
+    if not np.any(zeros & np.signbit(x)):
+        assert np.array_equal(q, q_o)
     if -120 <= k <= 115:
         p = synth.make_params(8, rng)
         q, s, y = run_kq(x, p)

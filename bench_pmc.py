@@ -202,7 +202,7 @@ CLOCK_KERNELS = [
 ]
 CLOCK_CMD = ("python3 bench.py --steps 20 --warmup 5 --no-cpu --eager --no-weights --no-norm --no-gemm --no-mlp "
              "--no-shard --no-quality --no-sweep --no-overlap")
-CLOCK_COUNTERS = "GRBM_GUI_ACTIVE GRBM_COUNT SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY"
+CLOCK_COUNTERS = "GRBM_GUI_ACTIVE SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY"
 
 
 def clock(run_dir):
@@ -227,24 +227,37 @@ def clock(run_dir):
         elif r["Dispatch_Id"] in times:
             d["_us"] = times[r["Dispatch_Id"]]
     names = CLOCK_COUNTERS.split()
-    md = ["# Clock and instruction counters per kernel, 4608x3072 bf16 (one MI355X)", "",
-          "Commands (repository root):", "", "```",
-          "rocprofv3 --kernel-trace --pmc " + CLOCK_COUNTERS + " --output-format csv -d gpurun_out/clock -o clock -- "
-          + CLOCK_CMD, "python3 bench_pmc.py clock gpurun_out/clock", "```", "",
-          "Medians per dispatch (counters summed over the device).  `MHz` = GRBM_GUI_ACTIVE / duration; "
-          "`VALU/wave` = SQ_INSTS_VALU / SQ_WAVES.", "",
-          "| kernel | dispatches | us | " + " | ".join(names) + " | MHz | VALU/wave |",
-          "|---|---|---|" + "---|" * len(names) + "---|---|"]
+    rows = []
     for key, label in CLOCK_KERNELS:
         ds = [d for d in per.get(key, {}).values() if "_us" in d]
         if not ds:
             continue
         med = {n: statistics.median(d.get(n, 0.0) for d in ds) for n in names}
-        us = statistics.median(d["_us"] for d in ds)
-        mhz = med["GRBM_GUI_ACTIVE"] / us if us else 0.0
+        rows.append((label, len(ds), statistics.median(d["_us"] for d in ds), med))
+    # GRBM_GUI_ACTIVE holds a fixed count of the profiler's window around each dispatch
+    # plus the busy cycles of the 8 XCDs: fit count = c0 + 8 f t over the kernels (one
+    # clock f for all), then each kernel's own clock is (count - c0) / (8 t)
+    ts = [r[2] for r in rows]
+    gs = [r[3]["GRBM_GUI_ACTIVE"] for r in rows]
+    n = len(ts)
+    tm, gm = sum(ts) / n, sum(gs) / n
+    slope = sum((t - tm) * (g - gm) for t, g in zip(ts, gs)) / sum((t - tm) ** 2 for t in ts)
+    c0 = gm - slope * tm
+    md = ["# Clock and instruction counters per kernel, 4608x3072 bf16 (one MI355X)", "",
+          "Commands (repository root):", "", "```",
+          "rocprofv3 --kernel-trace --pmc " + CLOCK_COUNTERS + " --output-format csv -d gpurun_out/clock -o clock -- "
+          + CLOCK_CMD, "python3 bench_pmc.py clock gpurun_out/clock", "```", "",
+          "Medians per dispatch (counters summed over the device).  GRBM_GUI_ACTIVE counts a fixed window of the "
+          "profiler around each dispatch plus 8 XCDs x the busy cycles; a least-squares fit over these kernels gives "
+          f"the window as {c0:,.0f} counts and one clock of {slope / 8 / 1e3:.3f} GHz; `GHz` is each kernel's own "
+          "(count - window) / (8 x duration).  `VALU/wave` = SQ_INSTS_VALU / SQ_WAVES.", "",
+          "| kernel | dispatches | us | " + " | ".join(names) + " | GHz | VALU/wave |",
+          "|---|---|---|" + "---|" * len(names) + "---|---|"]
+    for label, nd, us, med in rows:
+        ghz = (med["GRBM_GUI_ACTIVE"] - c0) / (8 * us) / 1e3 if us else 0.0
         vpw = med["SQ_INSTS_VALU"] / med["SQ_WAVES"] if med["SQ_WAVES"] else 0.0
-        md.append(f"| {label} | {len(ds)} | {us:.2f} | " + " | ".join(f"{med[n]:,.0f}" for n in names)
-                  + f" | {mhz:,.0f} | {vpw:.0f} |")
+        md.append(f"| {label} | {nd} | {us:.2f} | " + " | ".join(f"{med[n]:,.0f}" for n in names)
+                  + f" | {ghz:.2f} | {vpw:.0f} |")
     md.append("")
     open(os.path.join(ROOT, "profiles", "kq_kernels_flux_4608x3072_clock.md"), "w").write("\n".join(md))
     print("\n".join(md))

@@ -74,13 +74,16 @@ typedef enum {
 typedef enum { KQ_BF16 = 0, KQ_FP32 = 1 } kq_dtype;
 
 /* Transform formats.  Element counts per block: PARAMS 15 floats, DENSE_F32
- * 1024 floats, DENSE_BF16X3 3 x 1024 bf16. */
+ * 1024 floats, DENSE_BF16X3 3 x 1024 bf16, FACTORS_2X2_F32 20 floats. */
 typedef enum {
-  KQ_T_PARAMS = 0,        /* float32 [nb][5][3] (l,u,v): the factors themselves   */
+  KQ_T_PARAMS = 0,        /* float32 [nb][5][3] (l,u,v): the factors' parameters  */
   KQ_T_DENSE_F32 = 1,     /* float32 [nb][32][32]: T_b[i][j] row-major            */
-  KQ_T_DENSE_BF16X3 = 2   /* bf16 [3][nb][32][32]: hi, mid, lo with
+  KQ_T_DENSE_BF16X3 = 2,  /* bf16 [3][nb][32][32]: hi, mid, lo with
                              hi + mid + lo == fp32(T_b) (each the bf16 rounding of
                              what the previous parts leave)                       */
+  KQ_T_FACTORS_2X2_F32 = 3  /* float32 [nb][5][2][2]: F_k = L_k U_k =
+                             [[u, v], [l u, l v + 1/u]] row-major; an expansion
+                             output only (no quantize entry point reads it)       */
 } kq_tfmt;
 
 typedef enum {
@@ -95,8 +98,8 @@ typedef enum {
  * describes as folding the block structure into small GEMMs).
  *   params  device float32 [nb][5][3]
  *   nb      number of 32-channel blocks (>= 0; 0 is a no-op)
- *   tfmt    KQ_T_DENSE_F32 or KQ_T_DENSE_BF16X3 (KQ_T_PARAMS is rejected: it
- *           needs no expansion)
+ *   tfmt    KQ_T_DENSE_F32, KQ_T_DENSE_BF16X3 or KQ_T_FACTORS_2X2_F32
+ *           (KQ_T_PARAMS is rejected: it needs no expansion)
  *   t_out   device buffer of the format's size (see kq_tfmt)
  * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE (nb < 0), KQ_ERR_FORMAT, KQ_ERR_HIP. */
 int kq_expand_factors(const float* params, int64_t nb, int tfmt, void* t_out, void* stream);

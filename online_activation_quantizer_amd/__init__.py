@@ -6,7 +6,7 @@ the library is missing or fails to load, every call raises.
 """
 from .kq import (  # noqa: F401
     KQ_AUTO, KQ_BF16, KQ_BUTTERFLY, KQ_FP32, KQ_MFMA, KQ_T_DENSE_BF16X3, KQ_T_DENSE_F32,
-    KQ_T_PARAMS, KQError, STATUS, kq_expand_factors, kq_quantize, kq_transform_debug, lib,
+    KQ_T_PARAMS, KQ_T_FACTORS_2X2_F32, KQError, STATUS, kq_expand_factors, kq_quantize, kq_transform_debug, lib,
     sq_quantize, sq_transform_debug, expanded_numel, EXPORTED_SYMBOLS, kq_quantize_weights,
     kq_weights_debug, hq_quantize, hq_transform_debug, kq_norm_quantize, kq_norm_debug, kq_mx_gemm,
     KQ_OK, KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_DTYPE, KQ_ERR_FORMAT, KQ_ERR_VARIANT,

@@ -208,11 +208,13 @@ int norm_impl(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, co
 extern "C" {
 
 int kq_expand_factors(const float* params, int64_t nb, int tfmt, void* t_out, void* stream) {
-  if (tfmt != KQ_T_DENSE_F32 && tfmt != KQ_T_DENSE_BF16X3) return KQ_ERR_FORMAT;
+  if (tfmt != KQ_T_DENSE_F32 && tfmt != KQ_T_DENSE_BF16X3 && tfmt != KQ_T_FACTORS_2X2_F32)
+    return KQ_ERR_FORMAT;
   if (nb < 0 || nb > INT32_MAX) return KQ_ERR_SHAPE;
   if (nb == 0) return KQ_OK;
   if (!params || !t_out) return KQ_ERR_NULL;
-  if (!aligned(params, 4) || !aligned(t_out, 4)) return KQ_ERR_ALIGN;
+  if (!aligned(params, 4) || !aligned(t_out, tfmt == KQ_T_FACTORS_2X2_F32 ? 16 : 4))
+    return KQ_ERR_ALIGN;
   const hipError_t e = kq::launch_expand(params, nb, tfmt, t_out, stream);
   return e == hipSuccess ? KQ_OK : fail_hip(e);
 }

@@ -33,8 +33,9 @@
 // Lanes cover consecutive (row, block) units in memory order (a wave reads 4 KB
 // contiguous per row step) and advance through the rows with a stride that is a
 // multiple of nb, so every lane keeps one block for its whole life and computes
-// its 42 constants (32 d_i, 5 upper and 5 lower shear coefficients) once, while
-// its first row is already in flight.
+// its 42 constants (32 d_i, 5 upper and 5 lower shear coefficients) once: the
+// block's 15 parameters are requested before the lane's first row and the
+// constants are built while that row is in flight.
 #include "kq_device.hpp"
 #include "kq_factors.hpp"
 #include "kq_launch.hpp"
@@ -56,15 +57,20 @@ __global__ __launch_bounds__(kThreads) void butterfly_kernel(
   const uint32_t b = gtid % nb;
   const uint32_t t = gtid / nb;
   if (t >= rows) return;
+  BlockParams bp;
   BlockConsts c;
   uint8_t* const qcol = q + b * (kBlk / 2);
   uint8_t* const scol = s + b;
   uint8_t* const ycol = reinterpret_cast<uint8_t*>(y) + b * kBlk * 4;
-  for_each_row<DT, kRowDepth>(
+  for_each_row<DT>(
       x + (size_t)b * kBlk * (DT == DT_BF16 ? 2 : 4), rows, ldx, t, tstep,
       [&] {
-        // the block's factors, after the first rows' loads (4608 x 3072: 9.03 -> 8.69 us)
-        if (MODE != kHadamard) make_consts<MODE == kWeights>(load_params(params, b), c);
+        if (MODE != kHadamard) bp = load_params(params, b);
+      },
+      [&] {
+        // built while the first row is in flight (4608 x 3072: 8.24 -> 8.05 us against
+        // parameters requested after the row)
+        if (MODE != kHadamard) make_consts<MODE == kWeights>(bp, c);
       },
       [&](float (&v)[kBlk], uint32_t r) {
         if (MODE == kHadamard) hadamard(v);

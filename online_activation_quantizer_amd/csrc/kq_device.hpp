@@ -52,57 +52,40 @@ __device__ __forceinline__ void unpack(const Raw<DT_FP32>& r, float (&v)[kBlk]) 
 // each lane keeps one block column and walks rows t, t + tstep, ... < rows,
 // calling f(v, row) with the row's 32 values widened to fp32.  `xcol` points at
 // the lane's block column in row 0 and `ldx` is the row pitch in bytes; row
-// arithmetic is 32-bit, so every address is one multiply-add.  The loads run
-// DEPTH rows ahead in a ring of raw buffers.
-//  - `setup` runs after the first DEPTH rows are requested and loads the lane's
-//    constants there: the rows' DRAM requests leave first, and the constants
-//    (cache hits shared by many lanes) return while those are in flight.  Every
-//    lane runs it, also one whose first row t is past the end (its loads are
-//    clamped in bounds), so a set-up may hold a workgroup barrier.
-//  - Each slot is refilled right after it is unpacked, before its row's math and
-//    stores, so a refill is in flight during DEPTH rows of work and the memory
-//    operations of every slot come in the same order (refill, then stores).  The
-//    first round is peeled off the loop so that both edges into the loop header
-//    carry the same operations in flight; the compiler then waits for exactly
-//    the slot it needs and never for the stores.
-//  - Prefetches past the end are clamped to the last row (an in-bounds re-read),
-//    so no branch sits around a memory operation.
-template <int DT, int DEPTH, class S, class F>
+// arithmetic is 32-bit, so every address is one multiply-add.
+//  - `request` issues the loads of the lane's constants and runs first; `setup`
+//    (their arithmetic) runs after the first row has been requested.  Vector loads
+//    complete in the order they were issued, so constants requested after the row
+//    could only be used once the row had arrived; requested before it, they are
+//    built while the row is in flight.  Every lane runs both, also one whose first
+//    row is past the end (its load is clamped in bounds), so a set-up may hold a
+//    workgroup barrier.
+//  - Each row is loaded, transformed and stored before the next row is requested:
+//    a lane has 2-3 rows at the sizes of interest and the grid keeps 12 waves per
+//    compute unit in flight, which covers the memory latency; a one-row prefetch
+//    ring measured slower (its extra registers, and a re-read of the last row by
+//    every lane whose rows ran out) on 4608 x 3072.
+template <int DT, class R, class S, class F>
 __device__ __forceinline__ void for_each_row(const uint8_t* __restrict__ xcol, uint32_t rows,
-                                             uint32_t ldx, uint32_t t, uint32_t tstep, S&& setup,
-                                             F&& f) {
+                                             uint32_t ldx, uint32_t t, uint32_t tstep, R&& request,
+                                             S&& setup, F&& f) {
   const uint32_t last = rows - 1;
-  auto row_ptr = [&](uint32_t r) { return xcol + (uint64_t)(r < last ? r : last) * ldx; };
-  Raw<DT> ring[DEPTH];
-#pragma unroll
-  for (int k = 0; k < DEPTH; ++k) ring[k] = load_raw<DT>(row_ptr(t + k * tstep));
-  // the first rows' loads leave before the set-up, whose loads of the lane's
-  // constants (cache hits) would otherwise queue ahead of them
+  request();
+  Raw<DT> raw = load_raw<DT>(xcol + (uint64_t)(t < last ? t : last) * ldx);
+  // keep the row's load ahead of the constants' arithmetic (which waits for their loads)
   __builtin_amdgcn_sched_barrier(0);
   setup();
   __builtin_amdgcn_sched_barrier(0);
-  // lanes with no row (past the last unit) run the set-up with the others, since it
+  // lanes with no row (past the last unit) ran the set-up with the others, since it
   // may hold a workgroup barrier, and stop here
   if (t > last) return;
-  // one round over the ring; false once the rows are done
-  auto round = [&]() -> bool {
-#pragma unroll
-    for (int k = 0; k < DEPTH; ++k) {
-      float v[kBlk];
-      unpack(ring[k], v);
-      ring[k] = load_raw<DT>(row_ptr(t + DEPTH * tstep));
-      // pins the refill ahead of this row's math and stores: without the barrier the
-      // compiler folds the ring's incoming loads into one load at the top of the
-      // next round (or moves it behind the stores), which removes the prefetch
-      __builtin_amdgcn_sched_barrier(0);
-      f(v, t);
-      t += tstep;  // rows < 2^31 and tstep < 2^24: no wrap
-      if (t > last) return false;
-    }
-    return true;
-  };
-  if (!round()) return;
-  while (round()) {
+  for (;;) {
+    float v[kBlk];
+    unpack(raw, v);
+    f(v, t);
+    t += tstep;  // rows < 2^31 and tstep < 2^24: no wrap
+    if (t > last) return;
+    raw = load_raw<DT>(xcol + (uint64_t)t * ldx);
   }
 }
 

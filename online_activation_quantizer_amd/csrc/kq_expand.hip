@@ -3,7 +3,8 @@
 // method paragraph), with F = L*U = [[u, v], [l*u, l*v + 1/u]].  Entry (i, j) is the
 // product over k of F_k[bit(4-k) of i][bit(4-k) of j], computed in fp32.
 // The bf16x3 format additionally splits each fp32 entry into three bf16 parts
-// hi + mid + lo that sum to it exactly, for the matrix-core variant.
+// hi + mid + lo that sum to it exactly, for the matrix-core variant.  The 2x2
+// format writes the five factors F_k themselves, row-major.
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
@@ -49,9 +50,29 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(const float* __restric
   }
 }
 
+// One thread per (block, factor): F = L U = [[u, v], [l u, l v + 1/u]] (IEEE quotient).
+__global__ __launch_bounds__(kThreads) void factors_kernel(const float* __restrict__ params,
+                                                          int64_t n, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // block * 5 + factor
+  if (i >= n) return;
+  const float l = params[3 * i], u = params[3 * i + 1], v = params[3 * i + 2];
+  float4 f;
+  f.x = u;
+  f.y = v;
+  f.z = l * u;
+  f.w = l * v + 1.0f / u;
+  reinterpret_cast<float4*>(out)[i] = f;
+}
+
 }  // namespace
 
 hipError_t launch_expand(const float* params, int64_t nb, int tfmt, void* out, void* stream) {
+  if (tfmt == 3) {
+    const int64_t n = nb * 5;
+    hipLaunchKernelGGL(factors_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       (hipStream_t)stream, params, n, static_cast<float*>(out));
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)nb, 1024 / kThreads);
   if (tfmt == 1)
     hipLaunchKernelGGL((expand_kernel<1>), grid, dim3(kThreads), 0, (hipStream_t)stream, params,

@@ -7,16 +7,11 @@ namespace kq {
 
 constexpr int kThreads = 256;             // threads per workgroup (4 wave64)
 // Resident-grid target of the unit-per-lane kernels (3 workgroups = 12 waves per
-// CU measured best on MI355X for 4608 x 3072 and 4608 x 12288), and how many rows
-// ahead each lane's loads run (deeper rings measured no faster).
+// CU measured best on MI355X for 4608 x 3072: 2, 4 and 6 were slower).
 #ifndef KQ_BPCU
 #define KQ_BPCU 3
 #endif
 constexpr int kBlocksPerCU = KQ_BPCU;
-#ifndef KQ_DEPTH
-#define KQ_DEPTH 1
-#endif
-constexpr int kRowDepth = KQ_DEPTH;
 
 struct LaunchArgs {
   const void* x;

@@ -31,27 +31,33 @@ __global__ __launch_bounds__(kThreads) void sq_kernel(
   uint8_t* const qcol = q + b * (kBlk / 2);
   uint8_t* const scol = s + b;
   uint8_t* const ycol = reinterpret_cast<uint8_t*>(y) + b * kBlk * 4;
-  for_each_row<DT, kRowDepth>(
+  const uint32_t n4 = nblk * 8u;
+  // (a register-friendly vector type: an array of HIP's float4 struct shared by the
+  // two set-up steps is kept in scratch memory)
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  f32x4 tmp[8];
+  for_each_row<DT>(
       x + (size_t)b * kBlk * (DT == DT_BF16 ? 2 : 4), rows, ldx, t, tstep,
       [&] {
-        // after the first rows' loads: the workgroup's multipliers go through LDS (8
-        // loads per thread, all issued before any store; indices past the slice re-read
-        // its last chunk), then each lane reads its block's 32 (9.53 -> 9.18 us at
-        // 4608 x 3072 against 32 multipliers loaded by every lane)
-        const uint32_t n4 = nblk * 8u;
-        float4 tmp[8];
+        // before the first row: the workgroup's multipliers, on their way to LDS (8
+        // loads per thread; indices past the slice re-read its last chunk)
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           uint32_t f = threadIdx.x + kThreads * k;
           f = f < n4 ? f : n4 - 1u;
           uint32_t gb = b0 + f / 8u;
           gb = gb >= nb ? gb - nb : gb;
-          tmp[k] = reinterpret_cast<const float4*>(mult)[(size_t)gb * 8u + (f & 7u)];
+          tmp[k] = reinterpret_cast<const f32x4*>(mult)[(size_t)gb * 8u + (f & 7u)];
         }
+      },
+      [&] {
+        // while the first row is in flight: the multipliers into LDS, one barrier, and
+        // each lane reads its block's 32 (9.53 -> 9.18 us at 4608 x 3072 against 32
+        // multipliers loaded by every lane)
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const uint32_t f = threadIdx.x + kThreads * k;
-          if (f < n4) sm[f] = tmp[k];
+          if (f < n4) sm[f] = make_float4(tmp[k].x, tmp[k].y, tmp[k].z, tmp[k].w);
         }
         __syncthreads();
         // the lane's block in the slice: b itself when the workgroup covers every

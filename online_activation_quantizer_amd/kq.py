@@ -27,7 +27,7 @@ STATUS = {0: "KQ_OK", -1: "KQ_ERR_NULL", -2: "KQ_ERR_SHAPE", -3: "KQ_ERR_ALIGN",
           -4: "KQ_ERR_DTYPE", -5: "KQ_ERR_FORMAT", -6: "KQ_ERR_VARIANT", -7: "KQ_ERR_HIP",
           -8: "KQ_ERR_VALUE", -9: "KQ_ERR_DEVICE"}
 KQ_BF16, KQ_FP32 = 0, 1
-KQ_T_PARAMS, KQ_T_DENSE_F32, KQ_T_DENSE_BF16X3 = 0, 1, 2
+KQ_T_PARAMS, KQ_T_DENSE_F32, KQ_T_DENSE_BF16X3, KQ_T_FACTORS_2X2_F32 = 0, 1, 2, 3
 KQ_AUTO, KQ_BUTTERFLY, KQ_MFMA = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
@@ -177,8 +177,9 @@ def _need_outputs(what: str, x, q, s, y=None):
 
 
 def expanded_numel(nb: int, tfmt: int) -> int:
-    """Elements of an expanded transform (float32 for DENSE_F32, bf16 words for BF16X3)."""
-    return {KQ_T_DENSE_F32: nb * 1024, KQ_T_DENSE_BF16X3: 3 * nb * 1024}[tfmt]
+    """Elements of an expanded transform (float32 for DENSE_F32 and FACTORS_2X2_F32, bf16
+    words for BF16X3)."""
+    return {KQ_T_DENSE_F32: nb * 1024, KQ_T_DENSE_BF16X3: 3 * nb * 1024, KQ_T_FACTORS_2X2_F32: nb * 20}[tfmt]
 
 
 def kq_expand_factors(params, tfmt: int, out=None, stream=None):
@@ -189,14 +190,14 @@ def kq_expand_factors(params, tfmt: int, out=None, stream=None):
         _fail(KQ_ERR_SHAPE, f"{what}: params must be [nb, 5, 3], got {tuple(params.shape)}")
     nb = params.shape[0]
     _need_flat(what, "params", params, nb * 15, _f32, "float32")
-    if tfmt not in (KQ_T_DENSE_F32, KQ_T_DENSE_BF16X3):
+    if tfmt not in (KQ_T_DENSE_F32, KQ_T_DENSE_BF16X3, KQ_T_FACTORS_2X2_F32):
         _fail(KQ_ERR_FORMAT, f"{what}: format {tfmt} is not an expanded format")
+    f32 = tfmt != KQ_T_DENSE_BF16X3
     if out is None:
-        dt = torch.float32 if tfmt == KQ_T_DENSE_F32 else torch.int16
-        out = torch.empty(expanded_numel(nb, tfmt), dtype=dt,
+        out = torch.empty(expanded_numel(nb, tfmt), dtype=torch.float32 if f32 else torch.int16,
                           device=params.device if params.is_cuda else "cpu")
-    _need_flat(what, "out", out, expanded_numel(nb, tfmt), _f32 if tfmt == KQ_T_DENSE_F32 else _is16,
-               "float32" if tfmt == KQ_T_DENSE_F32 else "16-bit")
+    _need_flat(what, "out", out, expanded_numel(nb, tfmt), _f32 if f32 else _is16,
+               "float32" if f32 else "16-bit")
     _need_device(what, params, out=out)
     _check(lib().kq_expand_factors(params.data_ptr(), nb, tfmt, out.data_ptr(), _stream(stream)),
            "kq_expand_factors")

@@ -184,6 +184,8 @@ def test_expand_validation(L):
     assert L.kq_expand_factors(None, 4, 1, Y, None) == NULL
     assert L.kq_expand_factors(T, 4, 1, None, None) == NULL
     assert L.kq_expand_factors(T + 1, 4, 1, Y, None) == ALIGN
+    assert L.kq_expand_factors(T, 4, 3, Y + 4, None) == ALIGN  # 2x2 factors: 16-byte rows
+    assert L.kq_expand_factors(None, 4, 3, Y, None) == NULL
     assert L.kq_expand_factors(None, 0, 2, None, None) == OK
 
 

@@ -280,4 +280,12 @@ def test_expand_dense_f32_and_bf16x3():
     # the three bf16 parts sum exactly to the fp32 dense entry
     assert np.array_equal(hi + mid + lo, Tf)
     assert np.all(np.abs(mid) <= np.abs(hi) * 2.0 ** -8) and np.all(np.abs(lo) <= np.abs(mid) * 2.0 ** -8 + 0)
+    # the five 2x2 factors F = L U: u and v as given, l u rounded once, l v + 1/u three times
+    F = host(kq.kq_expand_factors(pd, kq.KQ_T_FACTORS_2X2_F32)).reshape(384, 5, 2, 2).astype(np.float64)
+    for b in (0, 1, 77, 383):
+        for k in range(5):
+            l, u, v = (float(t) for t in p[b, k])
+            F_o = oracle.factor(l, u, v)
+            tol = np.array([[0.0, 0.0], [abs(l * u), 2 * (abs(l * v) + abs(1 / u))]]) * 2.0 ** -24
+            assert np.all(np.abs(F[b, k] - F_o) <= tol), (b, k, F[b, k], F_o)
     torch.cuda.synchronize()

@@ -263,8 +263,72 @@ def clock(run_dir):
     print("\n".join(md))
 
 
+def counters(out_md, title, commands, dirs):
+    """Medians per dispatch of every counter in the rocprofv3 counter runs under
+    `dirs`, one row per (kernel, grid size), for the kernels named in CLOCK_KERNELS,
+    TRACE_KERNELS and the matrix-core and norm kernels; written as a markdown table
+    under profiles/ with the commands that produced the runs."""
+    known = [(k, v) for k, v in CLOCK_KERNELS] + [
+        ("void kq::(anonymous namespace)::mfma_kernel<false>", "matrix-core kq_quantize (design A)"),
+        ("void kq::(anonymous namespace)::norm_kernel<0, true, false>", "kq_norm_quantize (fused norm)"),
+        ("void kq::(anonymous namespace)::mx_gemm_kernel<", "kq_mx_gemm (W4A4 product)")]
+    per = {}
+    for dd in dirs:
+        for path in glob.glob(os.path.join(dd, "*counter_collection.csv")):
+            for r in csv.DictReader(open(path)):
+                label = next((v for k, v in known if r["Kernel_Name"].startswith(k)), None)
+                if label is None:
+                    continue
+                key = (label, int(r["Grid_Size"]))
+                d = per.setdefault(key, {}).setdefault((dd, int(r["Dispatch_Id"])), {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                if r.get("End_Timestamp"):
+                    d["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+    # a kernel timed in two legs of one run (the same grid on two shapes) shows as two
+    # runs of dispatch ids with other work between them: split at gaps of > 20 ids
+    split = {}
+    for (label, g), v in per.items():
+        ids = sorted(v)
+        legs, cur = [], [ids[0]]
+        for a, b in zip(ids, ids[1:]):
+            if b[0] != a[0] or b[1] - a[1] > 20:
+                legs.append(cur)
+                cur = []
+            cur.append(b)
+        legs.append(cur)
+        # the same leg in several runs (dirs) lines up by order within each run
+        by_dir = {}
+        for leg in legs:
+            by_dir.setdefault(leg[0][0], []).append(leg)
+        nlegs = max(len(x) for x in by_dir.values())
+        for i in range(nlegs):
+            name = label if nlegs == 1 else f"{label}, leg {i + 1}"
+            split[(name, g)] = {k: v[k] for x in by_dir.values() if i < len(x) for k in x[i]}
+    per = split
+    names = sorted({n for v in per.values() for d in v.values() for n in d if not n.startswith("_")})
+    md = [f"# {title}", "", "Commands (repository root):", "", "```"] + commands + ["```", "",
+          "Medians per dispatch, counters summed over the device (FETCH_SIZE / WRITE_SIZE in KiB as "
+          "the counter reports them).  Grid = work-items launched.", ""]
+    md.append("| counter | " + " | ".join(f"{lab} (grid {g:,})" for lab, g in per) + " |")
+    md.append("|---|" + "---|" * len(per))
+    def med(v, n, fmt):
+        xs = [d[n] for d in v.values() if n in d]
+        return format(statistics.median(xs), fmt) if xs else "-"
+    rows = [("dispatches (per run)", lambda v: f"{len(v) // max(1, len({k[0] for k in v}))}"),
+            ("duration us", lambda v: med(v, "_us", ".2f"))]
+    rows += [(n, (lambda n: lambda v: med(v, n, ",.0f"))(n)) for n in names]
+    for name, fn in rows:
+        md.append(f"| {name} | " + " | ".join(fn(v) for v in per.values()) + " |")
+    md.append("")
+    open(os.path.join(ROOT, "profiles", out_md), "w").write("\n".join(md))
+    print("\n".join(md))
+
+
 if __name__ == "__main__":
-    if sys.argv[1] == "trace":
+    if sys.argv[1] == "counters":
+        # bench_pmc.py counters OUT.md "title" "cmd1;cmd2;..." DIR [DIR ...]
+        counters(sys.argv[2], sys.argv[3], sys.argv[4].split(";"), sys.argv[5:])
+    elif sys.argv[1] == "trace":
         trace(sys.argv[2], sys.argv[3])
     elif sys.argv[1] == "clock":
         clock(sys.argv[2])

@@ -72,11 +72,13 @@ def test_45_degree_rotation_factors_match_hadamard_up_to_signs():
     those factors and the Hadamard path must give the same scales and the same code
     magnitudes (sign bits may differ), except where fp32 rounding of the two
     evaluation orders straddles a decision boundary.  Against the oracle: no
-    unexcused mismatch and the pre-quantization bound everywhere; the excused
-    count is held to 1e-3 of elements here, not the 1e-4 of the workloads' own
-    factors, because the rotations spread each block's outlier over all 32 values
-    (so the window, 1e-5 of the block's largest input, is wide next to them) and
-    the butterfly rounds five times where the Hadamard path's sums are exact."""
+    unexcused mismatch and the pre-quantization bound everywhere.  The excused
+    count is a known excess over the 1e-4 that every workload's own factors stay
+    under: 1,903 of 14,155,776 elements (1.34e-4), measured; this input and the
+    kernel's arithmetic are deterministic, so the assert holds it to 1.4e-4.  The
+    rotations spread each block's outlier over all 32 values (so the window, 1e-5
+    of the block's largest input, is wide next to them) and the butterfly rounds
+    five times where the Hadamard path's sums are exact."""
     import torch
     cfg = synth.get_config("flux")
     say("[rotation vs hadamard] flux")
@@ -96,4 +98,4 @@ def test_45_degree_rotation_factors_match_hadamard_up_to_signs():
     st = verdict(x, y_o, qk, sk, y_c=yk)
     say(f"  oracle: {st}")
     assert st["unexcused"] == 0 and st["prequant_violations"] == 0, st
-    assert st["excused"] < 1e-3 * st["elements"], st
+    assert st["excused"] <= 1.4e-4 * st["elements"], st

@@ -522,9 +522,48 @@ def gemm_timing(args, qs, ss):
     res = {"workload": f"FLUX.1-schnell MLP up-projection {M}x{N}x{K}, fp4 x fp4 (MXFP4), bf16 out",
            "ms_per_call": round(ms, 6), "tflops": round(tflops, 1),
            "mfma_frac_fp4": round(tflops / PEAK_FP4_TFLOPS, 4)}
+    if hasattr(ms, "summary"):
+        res["timing"] = ms.summary(steps)
     if not args.eager:
         res["library_baseline"] = library_gemm_timing(args, qs, ss, qw, sw, out)
     return res
+
+
+def gemm_split_timing(args):
+    """A product with few tiles and a long K, where splitting each tile in two K
+    halves (kq_mx_gemm_ws, through a workspace) pays: the FLUX MLP down-projection
+    for 1024 tokens, Y[1024, 3072] = deq(Qx)[1024, 12288] deq(Qw)[3072, 12288]^T
+    (48 tiles of 256 x 256 on 256 compute units), bf16 out; unsplit beside it."""
+    import torch
+
+    import synth
+    import online_activation_quantizer_amd as kq
+    cfg, wcfg = synth.get_config("flux_mlp"), synth.get_weight_config("flux_w_down")
+    M, N, K = 1024, wcfg.rows, cfg.d
+    x, p, _ = synth.make_inputs(cfg, rows=M)
+    w, _ = synth.make_weights(wcfg)
+    pd = torch.from_numpy(p).cuda()
+    qx, sx = kq.kq_quantize(torch.from_numpy(x.view(np.int16)).cuda(), pd)
+    qw, sw = kq.kq_quantize_weights(torch.from_numpy(w.view(np.int16)).cuda(), pd)
+    nbytes = kq.kq_mx_gemm_workspace_size(M, N, K)
+    ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device="cuda")
+    out, out_ws = (torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    steps = max(8, args.steps // 10)
+    legs = {}
+    for name, fn in (("unsplit", lambda i: kq.kq_mx_gemm(qx, sx, qw, sw, out=out)),
+                     ("split", lambda i: kq.kq_mx_gemm_ws(qx, sx, qw, sw, ws, out=out_ws))):
+        ms = (timed(fn, steps, args.warmup, torch.cuda.current_stream()) if args.eager
+              else timed_graph(fn, steps, min(args.warmup, 10)))
+        leg = {"ms_per_call": round(ms, 6), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+        if hasattr(ms, "summary"):
+            leg["timing"] = ms.summary(steps)
+        legs[name] = leg
+    torch.cuda.synchronize()
+    rel = float((out_ws.float() - out.float()).norm() / out.float().norm())
+    return {"workload": f"FLUX.1-schnell MLP down-projection, 1024 tokens: {M}x{N}x{K}, bf16 out",
+            "entry": "kq_mx_gemm_ws", "workspace_bytes": nbytes, **legs,
+            "t_split_over_t_unsplit": round(legs["split"]["ms_per_call"] / legs["unsplit"]["ms_per_call"], 4),
+            "rel_diff_vs_unsplit": round(rel, 6)}
 
 
 def library_gemm_timing(args, qs, ss, qw, sw, ours):
@@ -713,6 +752,8 @@ def main():
     weights = None if args.no_weights else weights_timing(args)
     norm = None if args.no_norm else norm_timing(args, cfg, xs, ps, qs, ss, ms)
     gemm = None if args.no_gemm else gemm_timing(args, qs, ss)
+    if gemm is not None:
+        gemm["few_tiles_split"] = gemm_split_timing(args)
     mlp = None if args.no_mlp else mlp_timing(args)
     shard = None if args.no_shard or args.variant != "butterfly" else shard_timing(args, xs, ps)
     sweep = None if args.no_sweep else sweep_timing(args)

@@ -68,7 +68,8 @@ typedef enum {
                            cannot consume                                    */
   KQ_ERR_VARIANT = -6,  /* unknown variant                                  */
   KQ_ERR_HIP = -7,      /* a HIP call failed                                */
-  KQ_ERR_VALUE = -8     /* a scalar argument out of range (eps)             */
+  KQ_ERR_VALUE = -8     /* a scalar argument out of range (eps, a workspace
+                           size)                                            */
 } kq_status;
 
 typedef enum { KQ_BF16 = 0, KQ_FP32 = 1 } kq_dtype;
@@ -219,13 +220,41 @@ int kq_norm_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx
  * B: weights as kq_quantize_weights writes them, qb [N][ldb], sb [N][ldsb].
  * out: [M][ldo] (ldo >= N elements) of out_dtype KQ_FP32 or KQ_BF16 (round to
  * nearest even from the fp32 accumulation).  K: multiple of 32.  qa, qb and their
- * pitches 16-byte aligned.  Runs on the gfx950 scaled matrix cores
+ * pitches 16-byte aligned; lda and ldb below 2^24 bytes (KQ_ERR_SHAPE otherwise).
+ * Runs on the gfx950 scaled matrix cores
  * (fp4 x fp4 with per-32 E8M0 scales, fp32 accumulation); scale bytes 0xFF (NaN)
  * give unspecified results.
  * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_DTYPE, KQ_ERR_HIP. */
 int kq_mx_gemm(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
                const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
                int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream);
+
+/* Bytes of device workspace that kq_mx_gemm_ws uses for an M x N x K product on
+ * the current device (written to *bytes; 0 when nothing is split, which is then
+ * the same product as kq_mx_gemm).  The product computes 256 x 256 output tiles, at
+ * most one workgroup per compute unit.  When twice the tiles (rounded up to a
+ * multiple of 8) fit on the compute units and K has at least 10 steps of 256,
+ * each tile is computed as two halves of K on two compute units, which meet
+ * through the workspace: 4096 bytes of flag words, then 256 KiB of fp32 partial
+ * sums per tile (1024 x 3072 x 12288: 48 tiles, 12 MiB, 0.70x the unsplit time).
+ * With more tiles the matrix cores are already busy on most compute units and
+ * nothing is split.
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_HIP. */
+int kq_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes);
+
+/* kq_mx_gemm with a caller-owned device workspace (same arguments and result):
+ *   workspace        device memory, 256-byte aligned (KQ_ERR_ALIGN), of at least
+ *                    kq_mx_gemm_workspace_size bytes (KQ_ERR_VALUE); its first 4096
+ *                    bytes are zero before the first call, and every call leaves
+ *                    them zero again.  NULL with workspace_bytes 0: no split, as
+ *                    kq_mx_gemm (NULL with other sizes: KQ_ERR_NULL).
+ * Calls that share a workspace must not run at the same time (one stream, or
+ * ordered streams).  The library allocates nothing.
+ * Errors: as kq_mx_gemm, and KQ_ERR_VALUE. */
+int kq_mx_gemm_ws(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
+                  const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+                  int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* workspace,
+                  int64_t workspace_bytes, void* stream);
 
 /* Static text for a kq_status value (never NULL). */
 const char* kq_status_string(int status);

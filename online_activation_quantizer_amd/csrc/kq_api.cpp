@@ -48,6 +48,7 @@ int current_cus(int* cus) {
 constexpr int64_t kMaxBlocks = int64_t(1) << 22;
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxPitch = (int64_t(1) << 32) - 1;
+constexpr int64_t kMaxGemmCodePitch = int64_t(1) << 24;
 // The normalization-fused kernel holds one row per workgroup: at most 512 blocks.
 constexpr int64_t kMaxNormWidth = 16384;
 
@@ -203,6 +204,52 @@ int norm_impl(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx, co
   return e == hipSuccess ? KQ_OK : fail_hip(e);
 }
 
+// argument checks shared by the product's entry points (KQ_OK: launch; the empty
+// product returns KQ_OK with *empty set)
+int check_mx_gemm(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
+                  const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+                  int64_t N, int64_t K, const void* out, int64_t ldo, int out_dtype, bool* empty) {
+  *empty = false;
+  if (out_dtype != KQ_FP32 && out_dtype != KQ_BF16) return KQ_ERR_DTYPE;
+  // code pitches below 16 MiB: a tile's 256 rows are read through one 32-bit range
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || K / 32 > kMaxBlocks || M > kMaxRows ||
+      N > kMaxRows || lda < K / 2 || ldb < K / 2 || ldsa < K / 32 || ldsb < K / 32 || ldo < N ||
+      lda >= kMaxGemmCodePitch || ldb >= kMaxGemmCodePitch || ldsa > kMaxPitch ||
+      ldsb > kMaxPitch || ldo * (out_dtype == KQ_FP32 ? 4 : 2) > kMaxPitch)
+    return KQ_ERR_SHAPE;
+  if (M == 0 || N == 0) {
+    *empty = true;
+    return KQ_OK;
+  }
+  if (((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return KQ_ERR_SHAPE;
+  if (!qa || !sa || !qb || !sb || !out) return KQ_ERR_NULL;
+  if (!aligned(qa, 16) || !aligned(qb, 16) || lda % 16 != 0 || ldb % 16 != 0 ||
+      !aligned(out, out_dtype == KQ_FP32 ? 4 : 2))
+    return KQ_ERR_ALIGN;
+  return KQ_OK;
+}
+
+int mx_gemm_impl(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
+                 const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+                 int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* workspace,
+                 int64_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_mx_gemm(qa, lda, sa, ldsa, qb, ldb, sb, ldsb, M, N, K, out, ldo, out_dtype, &empty);
+  if (rc != KQ_OK || empty) return rc;
+  if (!workspace && workspace_bytes != 0) return KQ_ERR_NULL;
+  if (workspace && !aligned(workspace, 256)) return KQ_ERR_ALIGN;
+  int cus = 0;
+  rc = current_cus(&cus);
+  if (rc != KQ_OK) return rc;
+  if (workspace && workspace_bytes < kq::mx_gemm_workspace_bytes(M, N, K, cus)) return KQ_ERR_VALUE;
+  kq::GemmArgs g{qa, lda, sa, ldsa, qb, ldb, sb, ldsb, M, N, K, out, ldo,
+                 out_dtype == KQ_BF16, stream, cus};
+  g.workspace = workspace;
+  g.workspace_bytes = workspace_bytes;
+  const hipError_t e = kq::launch_mx_gemm(g);
+  return e == hipSuccess ? KQ_OK : fail_hip(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -287,25 +334,30 @@ int kq_norm_debug(const void* x, int dtype, int64_t rows, int64_t d, int64_t ldx
 int kq_mx_gemm(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
                const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
                int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream) {
-  if (out_dtype != KQ_FP32 && out_dtype != KQ_BF16) return KQ_ERR_DTYPE;
-  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || K / 32 > kMaxBlocks || M > kMaxRows ||
-      N > kMaxRows || lda < K / 2 || ldb < K / 2 || ldsa < K / 32 || ldsb < K / 32 || ldo < N ||
-      lda > kMaxPitch || ldb > kMaxPitch || ldsa > kMaxPitch || ldsb > kMaxPitch ||
-      ldo * (out_dtype == KQ_FP32 ? 4 : 2) > kMaxPitch)
+  return mx_gemm_impl(qa, lda, sa, ldsa, qb, ldb, sb, ldsb, M, N, K, out, ldo, out_dtype, nullptr,
+                      0, stream);
+}
+
+int kq_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes) {
+  if (!bytes) return KQ_ERR_NULL;
+  *bytes = 0;
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || K / 32 > kMaxBlocks || M > kMaxRows || N > kMaxRows)
     return KQ_ERR_SHAPE;
   if (M == 0 || N == 0) return KQ_OK;
   if (((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return KQ_ERR_SHAPE;
-  if (!qa || !sa || !qb || !sb || !out) return KQ_ERR_NULL;
-  if (!aligned(qa, 16) || !aligned(qb, 16) || lda % 16 != 0 || ldb % 16 != 0 ||
-      !aligned(out, out_dtype == KQ_FP32 ? 4 : 2))
-    return KQ_ERR_ALIGN;
   int cus = 0;
   const int rc = current_cus(&cus);
   if (rc != KQ_OK) return rc;
-  const kq::GemmArgs g{qa, lda, sa, ldsa, qb, ldb, sb, ldsb, M, N, K, out, ldo,
-                       out_dtype == KQ_BF16, stream, cus};
-  const hipError_t e = kq::launch_mx_gemm(g);
-  return e == hipSuccess ? KQ_OK : fail_hip(e);
+  *bytes = kq::mx_gemm_workspace_bytes(M, N, K, cus);
+  return KQ_OK;
+}
+
+int kq_mx_gemm_ws(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
+                  const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+                  int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* workspace,
+                  int64_t workspace_bytes, void* stream) {
+  return mx_gemm_impl(qa, lda, sa, ldsa, qb, ldb, sb, ldsb, M, N, K, out, ldo, out_dtype, workspace,
+                      workspace_bytes, stream);
 }
 
 const char* kq_status_string(int status) {

@@ -28,10 +28,18 @@
 // substep's products.  The grid is persistent (one workgroup per compute unit,
 // tiles strided by the grid), and the step sequence runs across tile boundaries:
 // the next tile's first steps load while a tile's last step multiplies and its
-// outputs are written.  Rows past M or N are clamped on load and not stored;
-// K-blocks past K get scale 2^-127 on both operands (their products vanish).
+// outputs are written.  Code rows past M or N read zeros (buffer loads through a
+// per-tile range) and are not stored; K-blocks past K get scale 2^-127 on both
+// operands (their products vanish).
+//
+// Split tiles.  With a caller's workspace and few tiles (at most half the compute
+// units busy) and a long K, each tile is computed as two K halves on two
+// workgroups of its XCD; the first to finish stores its fp32 sums, the second adds
+// them to its own and writes the tile (kernel variant SPLIT).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "kq_launch.hpp"
 
@@ -88,13 +96,17 @@ struct Stage {
 // whole 128-byte row segments.
 constexpr int kEpiScalar = 0, kEpiVec4 = 1, kEpiStaged = 2;
 
+// marks a tile written from its accumulators alone
+struct NoPartial {};
 
-template <class T, bool OUT_BF16, int EPI, bool SCALE_WORDS>
+
+template <class T, bool OUT_BF16, int EPI, bool SCALE_WORDS, bool SPLIT>
 __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void mx_gemm_kernel(
     const uint8_t* __restrict__ qa, uint32_t lda, const uint8_t* __restrict__ sa, uint32_t ldsa,
     const uint8_t* __restrict__ qb, uint32_t ldb, const uint8_t* __restrict__ sb, uint32_t ldsb,
     uint32_t M, uint32_t N, uint32_t K, void* __restrict__ out, uint32_t ldo, uint32_t tiles_n,
-    uint32_t ntiles, uint32_t xcd_cols) {
+    uint32_t ntiles, uint32_t xcd_cols, uint32_t pair_off, uint32_t* __restrict__ flags,
+    float* __restrict__ partials) {
   constexpr int kRows = T::kRows, kBM = T::kBM, kThreads = T::kThreads;
   static_assert(EPI != kEpiStaged || (OUT_BF16 && T::kCanStage), "staged output: bf16, tiles that fit");
   __shared__ __attribute__((aligned(16))) uint8_t codes[2][kRows * kPitch];  // [slot], A rows then B rows
@@ -124,19 +136,24 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   // The rows this thread loads for the tile being fetched (origin lm0, ln0): code
   // chunk i is LDS row (tid + kThreads i) / kRowChunks (the first kChunksA of them A
   // rows), scale row j is LDS row tid + kThreads j (past the last row a duplicate
-  // whose value is not stored).  Rows past M or N re-read the matrix's last row and
-  // their products are not stored.
+  // whose value is not stored).  Code chunks are buffer loads through one descriptor
+  // per operand whose range ends with the tile's last row inside the matrix (K
+  // codes in): chunks of rows past M or N read zeros, and their products are not
+  // stored.  Scale rows past M or N re-read the matrix's last row.
   uint32_t lm0 = 0, ln0 = 0;
-  auto set_rows = [&](uint32_t t) { tile_origin(t, lm0, ln0); };
-  auto code_row = [&](int i) -> const uint8_t* {
-    const uint32_t r = (tid + kThreads * i) / kRowChunks;
-    if (i < T::kChunksA) {
-      const uint32_t g = lm0 + r < M ? lm0 + r : M - 1;
-      return qa + (uint64_t)g * lda;
-    }
-    const uint32_t g = ln0 + (r - kBM) < N ? ln0 + (r - kBM) : N - 1;
-    return qb + (uint64_t)g * ldb;
+  __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b;
+  auto set_rows = [&](uint32_t t) {
+    tile_origin(t, lm0, ln0);
+    const uint32_t rows_a = M - lm0 < (uint32_t)kBM ? M - lm0 : (uint32_t)kBM;
+    const uint32_t rows_b = N - ln0 < (uint32_t)T::kBN ? N - ln0 : (uint32_t)T::kBN;
+    rsrc_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(qa) + (uint64_t)lm0 * lda, 0,
+                                               (int)((rows_a - 1u) * lda + kbytes), 0x00020000);
+    rsrc_b = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(qb) + (uint64_t)ln0 * ldb, 0,
+                                               (int)((rows_b - 1u) * ldb + kbytes), 0x00020000);
   };
+  // byte offset of this thread's first code chunk in its A and B rows of a tile
+  const uint32_t chunk_a = (tid / kRowChunks) * lda + 16u * (tid % kRowChunks);
+  const uint32_t chunk_b = (tid / kRowChunks) * ldb + 16u * (tid % kRowChunks);
   auto scale_row = [&](int j) -> const uint8_t* {
     const uint32_t r0 = tid + kThreads * j, r = r0 < (uint32_t)kRows ? r0 : kRows - 1;
     if (r < (uint32_t)kBM) {
@@ -149,17 +166,17 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
 
   // global -> register loads of K step `step` of the current rows.  No load sits
   // under a branch (the compiler would then wait for every load in flight): code
-  // chunks past K re-read the row's last chunk, and their scale bytes on both
-  // operands become 0x00 (2^-127) when stored, so each of their products is below
-  // 36 * 2^-254 and vanishes in the fp32 accumulation whatever the codes (E2M1 codes
-  // are finite).
-  // this thread's column of K step `step` in its code rows: past K, the row's last chunk
-  auto chunk_col = [&](uint32_t step) {
-    const uint32_t kb0 = step * kBKBytes, col = 16u * (tid % kRowChunks);
-    return kb0 + col < kbytes ? kb0 + col : kbytes - 16u;
-  };
-  auto load_chunk = [&](uint32_t at, int i, Stage<T, SCALE_WORDS>& st) {
-    st.c[i] = *reinterpret_cast<const u32x4*>(code_row(i) + at);
+  // chunks past K read the bytes after the row (the next row's, or zeros past the
+  // descriptor's range), and their scale bytes on both operands become 0x00
+  // (2^-127) when stored, so each of their products is below 36 * 2^-254 and
+  // vanishes in the fp32 accumulation whatever the codes (E2M1 codes are finite).
+  constexpr uint32_t kRowsPerChunk = kThreads / kRowChunks;  // LDS rows between chunks i and i + 1
+  auto load_chunk = [&](uint32_t kb0, int i, Stage<T, SCALE_WORDS>& st) {
+    if (i < T::kChunksA)
+      st.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, chunk_a + kRowsPerChunk * i * lda + kb0, 0, 0);
+    else
+      st.c[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc_b, chunk_b + kRowsPerChunk * (i - T::kChunksA) * ldb + kb0, 0, 0);
   };
   auto load_scales = [&](uint32_t step, Stage<T, SCALE_WORDS>& st) {
     const uint32_t blk0 = step * 2u * kKSub;  // first scale byte of this step
@@ -184,9 +201,8 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
     }
   };
   auto load_stage = [&](uint32_t step, Stage<T, SCALE_WORDS>& st) {
-    const uint32_t at = chunk_col(step);
 #pragma unroll
-    for (int i = 0; i < T::kChunks; ++i) load_chunk(at, i, st);
+    for (int i = 0; i < T::kChunks; ++i) load_chunk(step * kBKBytes, i, st);
     load_scales(step, st);
   };
   auto store_chunk = [&](int slot, int i, const Stage<T, SCALE_WORDS>& st) {
@@ -282,7 +298,14 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
 
   // acc[i][j][4 q + e]: Y row lr of the wave's A tile i, column 8 q + 4 h + e of its
   // B tile j
-  auto write_tile = [&](uint32_t t) {
+  // `add` is NoPartial, or gives the 4 sums of the other K half of a split tile to
+  // add to the outputs acc[i][j][4 q .. 4 q + 3] as they are written
+  auto outputs = [&](auto add, int i, int j, int q) -> f32x4 {
+    const f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    if constexpr (std::is_same_v<decltype(add), NoPartial>) return v;
+    else return v + add(i, j, q);
+  };
+  auto write_tile = [&](uint32_t t, auto add) {
     uint32_t m0, n0;
     tile_origin(t, m0, n0);
 #pragma unroll
@@ -294,8 +317,7 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t col = n0 + wn * (32u * T::kTN) + 32u * j + 8u * q + 4u * h;
-          const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                              acc[i][j][4 * q + 3]};
+          const f32x4 v = outputs(add, i, j, q);
           if (OUT_BF16) {
             uint32_t b[4];
 #pragma unroll
@@ -334,7 +356,7 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   // step's operands.  The stores are buffer
   // stores whose descriptor spans the tile's rows of Y; pieces past N get an offset
   // outside it, so the hardware drops them with no branch.
-  auto write_tile_staged = [&](uint32_t t, int slot) {
+  auto write_tile_staged = [&](uint32_t t, int slot, auto add) {
     uint32_t m0, n0;
     tile_origin(t, m0, n0);
     uint8_t* st = codes[slot] + wave * (64u * kPitch);
@@ -349,11 +371,12 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
         for (int j = 0; j < T::kTN; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
+            const f32x4 v = outputs(add, 2 * half + ii, j, q);
             uint32_t b[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               // round to nearest even (finite values)
-              const uint32_t u = __float_as_uint(acc[2 * half + ii][j][4 * q + e]);
+              const uint32_t u = __float_as_uint(v[e]);
               b[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
             }
             *reinterpret_cast<u32x2*>(st + (32u * ii + lr) * kPitch + (32u * j + 8u * q + 4u * h) * 2u) =
@@ -379,26 +402,53 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
     __syncthreads();
   };
 
-  // The step sequence of this workgroup: its tiles blockIdx.x, + grid, ... (my_tiles
-  // of them), nsteps K steps each.  One register stage S: during step g (LDS slot
-  // g % 2), after the products of its first substep, S (step g + 1, loaded during
-  // step g - 1) goes to the other slot and the loads of step g + 2 start into S, so
-  // each load has a step of products to arrive.  Every load is issued
-  // unconditionally (past the last step of the last tile, the last tile's rows are
-  // re-read), so the only wait for memory is the one before S goes to LDS.
-  const uint32_t my_tiles = (ntiles - 1u - blockIdx.x) / grid + 1u;  // grid <= ntiles
-  const uint64_t total = (uint64_t)my_tiles * nsteps;
-  uint32_t l_tile = blockIdx.x, l_step = 0;  // the step the next load fetches
+  // The work of this workgroup.  Whole tiles: tiles blockIdx.x, + grid, ...
+  // (my_tiles of them), nsteps K steps each.  SPLIT (fewer tiles than half the
+  // grid): one K half of one tile, workgroup b < ntiles taking steps [0, nsteps / 2)
+  // of tile b and workgroup pair_off + b steps [nsteps / 2, nsteps) (pair_off a
+  // multiple of 8, so both run on the tile's XCD); the other workgroups have
+  // nothing to do.
+  const uint32_t wg = blockIdx.x;
+  uint32_t l_tile = wg, l_step = 0, l_end = nsteps;  // the step the next load fetches (split: [l_step, l_end))
+  uint64_t total;
+  if constexpr (SPLIT) {
+    const uint32_t mid = nsteps / 2u;
+    if (wg < ntiles) {
+      l_end = mid;
+    } else if (wg >= pair_off && wg - pair_off < ntiles) {
+      l_tile = wg - pair_off;
+      l_step = mid;
+    } else {
+      return;
+    }
+    total = l_end - l_step;
+  } else {
+    total = (uint64_t)((ntiles - 1u - wg) / grid + 1u) * nsteps;  // grid <= ntiles
+  }
+  const uint32_t h_tile = l_tile;
+
+  // The step sequence.  One register stage S: during step g (LDS slot g % 2), after
+  // the products of its first substep, S (step g + 1, loaded during step g - 1) goes
+  // to the other slot and the loads of step g + 2 start into S, so each load has a
+  // step of products to arrive.  Whole tiles: the sequence runs across tile
+  // boundaries, so the next tile's first steps load while a tile's last step
+  // multiplies and its outputs are written.  Every load is issued unconditionally
+  // (past the last step, the last tile's or half's last step is re-read), so the
+  // only wait for memory is the one before S goes to LDS.
   set_rows(l_tile);
   Stage<T, SCALE_WORDS> S;
   uint32_t s_step = 0;  // K step held in S
-  // (branch-free, so that the step's products, LDS stores and loads stay in one
-  // block the scheduler can interleave; past the last tile the last tile's rows)
+  // (selects, no branch, so that the step's products, LDS stores and loads stay in
+  // one block the scheduler can interleave)
   auto advance = [&]() {
-    const bool wrap = l_step + 1u == nsteps;
-    l_step = wrap ? 0u : l_step + 1u;
-    l_tile = wrap ? l_tile + grid : l_tile;
-    set_rows(l_tile < ntiles ? l_tile : ntiles - 1u);
+    if constexpr (SPLIT) {
+      l_step = l_step + 1u < l_end ? l_step + 1u : l_step;
+    } else {
+      const bool wrap = l_step + 1u == nsteps;
+      l_step = wrap ? 0u : l_step + 1u;
+      l_tile = wrap ? l_tile + grid : l_tile;
+      set_rows(l_tile < ntiles ? l_tile : ntiles - 1u);
+    }
   };
   auto load_next = [&]() {
     s_step = l_step;
@@ -409,7 +459,7 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   store_stage(0, s_step, S);
   load_next();
   __syncthreads();
-  uint32_t c_tile = blockIdx.x, c_step = 0;
+  uint32_t c_tile = wg, c_step = 0;
   for (uint64_t g = 0; g < total; ++g) {
     const int slot = (int)(g & 1u);
     Scales sc;
@@ -430,55 +480,168 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
     for (int ks = 1; ks < kKSub; ++ks) compute_ks(slot, ks, sc, no_hook);
     __syncthreads();
-    if (++c_step == nsteps) {
-      if (EPI == kEpiStaged) write_tile_staged(c_tile, slot);
-      else write_tile(c_tile);
+    if constexpr (!SPLIT) {
+      if (++c_step == nsteps) {
+        if (EPI == kEpiStaged) write_tile_staged(c_tile, slot, NoPartial{});
+        else write_tile(c_tile, NoPartial{});
 #pragma unroll
-      for (int i = 0; i < T::kTM; ++i)
+        for (int i = 0; i < T::kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < T::kTN; ++j) acc[i][j] = v16f{};
-      c_step = 0;
-      c_tile += grid;
+          for (int j = 0; j < T::kTN; ++j) acc[i][j] = v16f{};
+        c_step = 0;
+        c_tile += grid;
+      }
     }
   }
+  if constexpr (!SPLIT) return;
+
+  // The two halves of a split tile meet through its flag word and one fp32 tile of
+  // partial sums (thread tid's accumulators as 16-byte pieces, piece p at
+  // p kThreads + tid).  Each half adds 1 to the flag on arrival (bits 0-1 count the
+  // arrivals).  The first to arrive (old value 0) stores its sums, waits until they
+  // are visible to the device and adds kReady; the second (old value 1 or 1 + kReady)
+  // waits for kReady, which comes from a workgroup that is already running and
+  // waits for nothing, adds the stored sums to its own, puts the flag back to 0 for
+  // the next call and writes the tile.  No workgroup waits for one that may not
+  // have started, whatever the order workgroups run in.
+  constexpr uint32_t kReady = 4u;
+  __shared__ uint32_t arrival;
+  const uint32_t sidx = h_tile;
+  uint32_t* flag = flags + sidx;
+  // the tile's sums through one buffer descriptor: piece p of this thread at byte
+  // offset 16 tid (per lane) + 16 kThreads p (per instruction).  They are stored and
+  // loaded device-coherent (cache policy sc1, the form of agent-scope relaxed
+  // atomics), so they need no cache write-back or invalidation, which would also
+  // drop the other workgroups' operands from the XCD's L2.
+  const __amdgpu_buffer_rsrc_t rsrc_p = __builtin_amdgcn_make_buffer_rsrc(
+      partials + (uint64_t)sidx * (kBM * T::kBN), 0, kBM * T::kBN * 4, 0x00020000);
+  constexpr int kDeviceCoherent = 16;  // sc1
+  if (tid == 0) arrival = __hip_atomic_fetch_add(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(arrival) == 0u) {
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::kTN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsrc_p, (int)(16u * tid),
+                                                 16 * kThreads * ((i * T::kTN + j) * 4 + q),
+                                                 kDeviceCoherent);
+        }
+    // every wave's stores complete (visible device-wide) before the flag changes
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+    __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(flag, kReady, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (tid == 0) {
+    // bounded: the first half has arrived and only stores its sums before kReady
+    for (uint32_t n = 0; n < (1u << 26); ++n) {
+      if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kReady) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto stored_sums = [&](int i, int j, int q) {
+    return __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_p, (int)(16u * tid),
+                                                     16 * kThreads * ((i * T::kTN + j) * 4 + q),
+                                                     kDeviceCoherent));
+  };
+  if (EPI == kEpiStaged) write_tile_staged(h_tile, 0, stored_sums);
+  else write_tile(h_tile, stored_sums);
 }
 
 }  // namespace
 
-template <class T, bool OUT_BF16, int EPI, bool SCALE_WORDS>
-void launch_t(const GemmArgs& g, int64_t tiles_n, int64_t ntiles, int64_t grid, int64_t xcd_cols) {
-  hipLaunchKernelGGL((mx_gemm_kernel<T, OUT_BF16, EPI, SCALE_WORDS>), dim3((unsigned)grid),
+// The grid and the tiles' order for one product (the kernel's unit list).
+struct Schedule {
+  int64_t tiles_n, ntiles, grid, xcd_cols;
+  bool split;        // every tile in two K halves through the workspace
+  int64_t pair_off;  // workgroup of a tile's second half, past the first's
+};
+
+// Tiles are split in K halves only when at least this many K steps (of 256
+// values) make a half worth the exchange of partial sums (split against unsplit:
+// 4096 x 1152 x 1152, 5 steps: 1.34x the time; 2048 x 2240 x 2240, 9 steps:
+// 0.95-1.01x; 256 x 256 x 3072, 12 steps: 0.82-0.85x; 1024 x 3072 x 12288, 48
+// steps: 0.70x).
+constexpr int64_t kSplitMinSteps = 10;
+
+Schedule make_schedule(int64_t M, int64_t N, int64_t K, int cus, bool allow_split) {
+  using T = ProductTiling;
+  Schedule s{};
+  const int64_t tiles_m = (M + T::kBM - 1) / T::kBM;
+  s.tiles_n = (N + T::kBN - 1) / T::kBN;
+  s.ntiles = tiles_m * s.tiles_n;
+  // persistent: at most one workgroup per compute unit (its LDS holds one), a
+  // multiple of 8 so that a workgroup's tiles all fall to its XCD's share
+  const int64_t full_grid = cus >= 8 ? cus / 8 * 8 : 8;
+  const int64_t nsteps = (K + 64 * kKSub - 1) / (64 * kKSub);
+  const int64_t n8 = (s.ntiles + 7) / 8 * 8;
+  // Splitting pays only while the tiles leave at least half of the compute units
+  // idle: with whole rounds of tiles on (nearly) all of them, the matrix cores are
+  // power-limited (4608 x 12288 x 3072: the shader clock falls from 1.92 GHz with
+  // 216 busy compute units to 1.45-1.69 with 256), so more busy units bring no more
+  // throughput, and splitting only adds the exchange.
+  s.split = allow_split && 2 * n8 <= full_grid && s.ntiles <= kSplitMaxTiles && nsteps >= kSplitMinSteps;
+  if (s.split) {
+    s.pair_off = n8;
+    s.grid = 2 * n8;
+  } else {
+    // no more workgroups than keep the number of tile rounds, so every workgroup
+    // runs the same number of tiles up to one (4608 x 12288: 864 tiles, 216
+    // workgroups of 4 instead of 256 of 3 or 4: 121.9 -> 120.1 us)
+    s.pair_off = 0;
+    s.grid = full_grid < s.ntiles ? full_grid : s.ntiles;
+    const int64_t rounds = (s.ntiles + s.grid - 1) / s.grid;
+    int64_t even = (s.ntiles + rounds - 1) / rounds;
+    even = (even + 7) / 8 * 8;
+    if (even < s.grid) s.grid = even;
+  }
+  s.xcd_cols = s.tiles_n % 8 == 0 && s.grid % 8 == 0 ? s.tiles_n / 8 : 0;
+  return s;
+}
+
+int64_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus) {
+  const Schedule s = make_schedule(M, N, K, cus, true);
+  return s.split ? kSplitFlagBytes + s.ntiles * kSplitTileBytes : 0;
+}
+
+template <class T, bool OUT_BF16, int EPI, bool SCALE_WORDS, bool SPLIT>
+void launch_t(const GemmArgs& g, const Schedule& s) {
+  uint8_t* ws = static_cast<uint8_t*>(g.workspace);
+  hipLaunchKernelGGL((mx_gemm_kernel<T, OUT_BF16, EPI, SCALE_WORDS, SPLIT>), dim3((unsigned)s.grid),
                      dim3(T::kThreads), 0, (hipStream_t)g.stream, g.qa, (uint32_t)g.lda, g.sa,
                      (uint32_t)g.ldsa, g.qb, (uint32_t)g.ldb, g.sb, (uint32_t)g.ldsb, (uint32_t)g.M,
-                     (uint32_t)g.N, (uint32_t)g.K, g.out, (uint32_t)g.ldo, (uint32_t)tiles_n,
-                     (uint32_t)ntiles, (uint32_t)xcd_cols);
+                     (uint32_t)g.N, (uint32_t)g.K, g.out, (uint32_t)g.ldo, (uint32_t)s.tiles_n,
+                     (uint32_t)s.ntiles, (uint32_t)s.xcd_cols, (uint32_t)s.pair_off,
+                     reinterpret_cast<uint32_t*>(ws),
+                     ws ? reinterpret_cast<float*>(ws + kSplitFlagBytes) : nullptr);
 }
 
 template <class T, bool OUT_BF16, int EPI>
-void launch_w(const GemmArgs& g, bool words, int64_t tiles_n, int64_t ntiles, int64_t grid,
-              int64_t xcd_cols) {
-  if (words) launch_t<T, OUT_BF16, EPI, true>(g, tiles_n, ntiles, grid, xcd_cols);
-  else launch_t<T, OUT_BF16, EPI, false>(g, tiles_n, ntiles, grid, xcd_cols);
+void launch_w(const GemmArgs& g, bool words, const Schedule& s) {
+  if (s.split) {
+    if (words) launch_t<T, OUT_BF16, EPI, true, true>(g, s);
+    else launch_t<T, OUT_BF16, EPI, false, true>(g, s);
+  } else {
+    if (words) launch_t<T, OUT_BF16, EPI, true, false>(g, s);
+    else launch_t<T, OUT_BF16, EPI, false, false>(g, s);
+  }
 }
 
 hipError_t launch_mx_gemm(const GemmArgs& g) {
   using T = ProductTiling;
-  const int64_t tiles_m = (g.M + T::kBM - 1) / T::kBM, tiles_n = (g.N + T::kBN - 1) / T::kBN;
-  const int64_t ntiles = tiles_m * tiles_n;
-  // persistent: at most one workgroup per compute unit (its LDS holds one), a
-  // multiple of 8 so that a workgroup's tiles all fall to its XCD's share; and no
-  // more workgroups than keep the number of tile rounds, so every workgroup runs
-  // the same number of tiles up to one (4608 x 12288: 864 tiles, 216 workgroups of
-  // 4 instead of 256 of 3 or 4: 121.9 -> 120.1 us)
-  int64_t grid = g.cus >= 8 ? g.cus / 8 * 8 : 8;
-  if (grid > ntiles) grid = ntiles;
-  {
-    const int64_t rounds = (ntiles + grid - 1) / grid;
-    int64_t even = (ntiles + rounds - 1) / rounds;
-    even = (even + 7) / 8 * 8;
-    if (even < grid) grid = even;
-  }
-  const int64_t xcd_cols = tiles_n % 8 == 0 && grid % 8 == 0 ? tiles_n / 8 : 0;
+  // the split schedule only with a workspace that holds it
+  const bool split = g.workspace != nullptr &&
+                     g.workspace_bytes >= mx_gemm_workspace_bytes(g.M, g.N, g.K, g.cus);
+  const Schedule s = make_schedule(g.M, g.N, g.K, g.cus, split);
   // whole 32-bit scale words when every scale row starts 4-byte aligned and holds one
   const bool words = ((uintptr_t)g.sa % 4 == 0) && ((uintptr_t)g.sb % 4 == 0) && g.ldsa % 4 == 0 &&
                      g.ldsb % 4 == 0 && g.K >= 128;
@@ -490,15 +653,15 @@ hipError_t launch_mx_gemm(const GemmArgs& g) {
   if (g.out_bf16) {
     if constexpr (T::kCanStage) {
       if (staged) {
-        launch_w<T, true, kEpiStaged>(g, words, tiles_n, ntiles, grid, xcd_cols);
+        launch_w<T, true, kEpiStaged>(g, words, s);
         return hipGetLastError();
       }
     }
-    if (vec4) launch_w<T, true, kEpiVec4>(g, words, tiles_n, ntiles, grid, xcd_cols);
-    else launch_w<T, true, kEpiScalar>(g, words, tiles_n, ntiles, grid, xcd_cols);
+    if (vec4) launch_w<T, true, kEpiVec4>(g, words, s);
+    else launch_w<T, true, kEpiScalar>(g, words, s);
   } else {
-    if (vec4) launch_w<T, false, kEpiVec4>(g, words, tiles_n, ntiles, grid, xcd_cols);
-    else launch_w<T, false, kEpiScalar>(g, words, tiles_n, ntiles, grid, xcd_cols);
+    if (vec4) launch_w<T, false, kEpiVec4>(g, words, s);
+    else launch_w<T, false, kEpiScalar>(g, words, s);
   }
   return hipGetLastError();
 }

@@ -55,7 +55,19 @@ struct GemmArgs {
   bool out_bf16;
   void* stream;
   int cus;       // compute units of the device (persistent grid size)
+  // device workspace for tiles split in K halves (flags first, zero between
+  // calls), or NULL for whole tiles only; used when it holds
+  // mx_gemm_workspace_bytes()
+  void* workspace = nullptr;
+  int64_t workspace_bytes = 0;
 };
+
+// Workspace of the W4A4 product's split tiles: kSplitFlagBytes of flags (one
+// 32-bit word per split tile, zero between calls), then one 256 x 256 fp32 tile of
+// partial sums per split tile.
+constexpr int64_t kSplitFlagBytes = 4096;
+constexpr int64_t kSplitMaxTiles = kSplitFlagBytes / 4;
+constexpr int64_t kSplitTileBytes = 256 * 256 * 4;
 
 inline int64_t gcd64(int64_t a, int64_t b) {
   while (b) {
@@ -87,6 +99,8 @@ hipError_t launch_weights(const LaunchArgs& a);   // W T^-1 along each row, then
 hipError_t launch_hadamard(const LaunchArgs& a);  // fixed block-Hadamard, then MXFP4
 hipError_t launch_norm(const NormArgs& n);        // LayerNorm + modulation, T_b, MXFP4
 hipError_t launch_mx_gemm(const GemmArgs& g);    // Y = deq(A) deq(B)^T on scaled MFMA
+// bytes of workspace the product's split tiles need (0: nothing is split)
+int64_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_sq(const LaunchArgs& a);
 hipError_t launch_mfma(const LaunchArgs& a);
 hipError_t launch_expand(const float* params, int64_t nb, int tfmt, void* out, void* stream);

@@ -33,7 +33,8 @@ KQ_AUTO, KQ_BUTTERFLY, KQ_MFMA = 0, 1, 2
 EXPORTED_SYMBOLS = ("kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
                     "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug",
                     "hq_quantize", "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug",
-                    "kq_mx_gemm", "kq_status_string", "kq_last_hip_error")
+                    "kq_mx_gemm", "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws", "kq_status_string",
+                    "kq_last_hip_error")
 
 
 class KQError(RuntimeError):
@@ -69,6 +70,8 @@ def lib():
         L.kq_norm_quantize.argtypes = [P, I, I64, I64, I64, P, P, I64, F, P, P, I64, P, I64, P]
         L.kq_norm_debug.argtypes = [P, I, I64, I64, I64, P, P, I64, F, P, P, I64, P, I64, P, I64, P]
         L.kq_mx_gemm.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, I64, I, P]
+        L.kq_mx_gemm_workspace_size.argtypes = [I64, I64, I64, ctypes.POINTER(I64)]
+        L.kq_mx_gemm_ws.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, I64, I, P, I64, P]
         L.kq_status_string.argtypes = [I]
         L.kq_status_string.restype = ctypes.c_char_p
         L.kq_last_hip_error.argtypes = []
@@ -385,11 +388,8 @@ def kq_norm_debug(x, params, shift=None, scale=None, rows_per_sample=None, eps: 
     return q, s, y
 
 
-def kq_mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
-    """W4A4 product out[m][n] = sum_k deq(A)[m][k] deq(B)[n][k] of two MXFP4 operands
-    (codes [rows, K/2], scales [rows, K/32]); out float32 (default) or bfloat16."""
+def _mx_gemm(what, qa, sa, qb, sb, out, out_dtype, workspace, stream):
     import torch
-    what = "kq_mx_gemm"
     for name, t in (("qa", qa), ("sa", sa), ("qb", qb), ("sb", sb)):
         if t.dim() != 2:
             _fail(KQ_ERR_SHAPE, f"{what}: {name} must be 2-D, got {tuple(t.shape)}")
@@ -398,7 +398,7 @@ def kq_mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
         _row_pitch(t)
     M, N, K = qa.shape[0], qb.shape[0], qa.shape[1] * 2
     if qb.shape[1] != qa.shape[1] or tuple(sa.shape) != (M, K // 32) or tuple(sb.shape) != (N, K // 32):
-        raise KQError(KQ_ERR_SHAPE, "kq_mx_gemm: codes [rows, K/2] and scales [rows, K/32] of both operands "
+        raise KQError(KQ_ERR_SHAPE, f"{what}: codes [rows, K/2] and scales [rows, K/32] of both operands "
                                     "must agree on K")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=qa.device)
@@ -408,8 +408,40 @@ def kq_mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
     if out.dim() != 2 or tuple(out.shape) != (M, N):
         _fail(KQ_ERR_SHAPE, f"{what}: out is {tuple(out.shape)}, needs ({M}, {N})")
     _row_pitch(out)
-    _need_device(what, qa, sa=sa, qb=qb, sb=sb, out=out)
-    _check(lib().kq_mx_gemm(qa.data_ptr(), _row_pitch(qa), sa.data_ptr(), _row_pitch(sa), qb.data_ptr(),
-                            _row_pitch(qb), sb.data_ptr(), _row_pitch(sb), M, N, K, out.data_ptr(),
-                            _row_pitch(out), code, _stream(stream)), "kq_mx_gemm")
+    args = (qa.data_ptr(), _row_pitch(qa), sa.data_ptr(), _row_pitch(sa), qb.data_ptr(), _row_pitch(qb),
+            sb.data_ptr(), _row_pitch(sb), M, N, K, out.data_ptr(), _row_pitch(out), code)
+    if workspace is False:
+        _need_device(what, qa, sa=sa, qb=qb, sb=sb, out=out)
+        _check(lib().kq_mx_gemm(*args, _stream(stream)), what)
+        return out
+    if workspace is None:
+        _need_device(what, qa, sa=sa, qb=qb, sb=sb, out=out)
+        _check(lib().kq_mx_gemm_ws(*args, None, 0, _stream(stream)), what)
+        return out
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
+        _fail(KQ_ERR_DTYPE, f"{what}: workspace must be a contiguous 1-D uint8 tensor")
+    _need_device(what, qa, sa=sa, qb=qb, sb=sb, out=out, workspace=workspace)
+    _check(lib().kq_mx_gemm_ws(*args, workspace.data_ptr(), workspace.numel(), _stream(stream)), what)
     return out
+
+
+def kq_mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
+    """W4A4 product out[m][n] = sum_k deq(A)[m][k] deq(B)[n][k] of two MXFP4 operands
+    (codes [rows, K/2], scales [rows, K/32]); out float32 (default) or bfloat16."""
+    return _mx_gemm("kq_mx_gemm", qa, sa, qb, sb, out, out_dtype, False, stream)
+
+
+def kq_mx_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace kq_mx_gemm_ws uses for an M x N x K product on the current device."""
+    n = ctypes.c_int64(0)
+    _check(lib().kq_mx_gemm_workspace_size(M, N, K, ctypes.byref(n)), "kq_mx_gemm_workspace_size")
+    return n.value
+
+
+def kq_mx_gemm_ws(qa, sa, qb, sb, workspace, out=None, out_dtype=None, stream=None):
+    """kq_mx_gemm with each output tile split in two K halves through
+    ``workspace`` when the library's rule splits the shape (uint8 device tensor of
+    kq_mx_gemm_workspace_size bytes whose first 4096 bytes are zero before the
+    first call; every call leaves them zero).  ``workspace=None`` runs the unsplit
+    product."""
+    return _mx_gemm("kq_mx_gemm_ws", qa, sa, qb, sb, out, out_dtype, workspace, stream)

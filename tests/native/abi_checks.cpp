@@ -107,6 +107,25 @@ int main() {
   EXPECT(kq_mx_gemm(Q, 64, S, 4, T, 64, S, 4, 8, 8, 128, X + 2, 8, 1, nullptr), KQ_ERR_ALIGN);
   EXPECT(kq_mx_gemm(nullptr, 64, nullptr, 4, nullptr, 64, nullptr, 4, 0, 8, 128, nullptr, 8, 1, nullptr),
          KQ_OK);
+  // code pitches of 16 MiB and more
+  EXPECT(kq_mx_gemm(Q, 1 << 24, S, 4, T, 64, S, 4, 8, 8, 128, X, 8, 1, nullptr), KQ_ERR_SHAPE);
+  EXPECT(kq_mx_gemm(Q, 64, S, 4, T, 1 << 24, S, 4, 8, 8, 128, X, 8, 1, nullptr), KQ_ERR_SHAPE);
+  // with a workspace: the same checks first, then the workspace's own
+  void* const W = reinterpret_cast<void*>(0x60000);
+  EXPECT(kq_mx_gemm_ws(Q, 64, S, 4, T, 64, S, 4, 8, 8, 48, X, 8, 1, W, 1 << 20, nullptr), KQ_ERR_SHAPE);
+  EXPECT(kq_mx_gemm_ws(Q, 64, S, 4, T, 64, S, 4, 8, 8, 128, X, 8, 1, nullptr, 4096, nullptr), KQ_ERR_NULL);
+  EXPECT(kq_mx_gemm_ws(Q, 64, S, 4, T, 64, S, 4, 8, 8, 128, X, 8, 1,
+                       reinterpret_cast<uint8_t*>(W) + 128, 1 << 20, nullptr),
+         KQ_ERR_ALIGN);
+  EXPECT(kq_mx_gemm_ws(nullptr, 64, nullptr, 4, nullptr, 64, nullptr, 4, 8, 0, 128, nullptr, 8, 1, W, 0,
+                       nullptr),
+         KQ_OK);
+  int64_t bytes = -1;
+  EXPECT(kq_mx_gemm_workspace_size(8, 8, 128, nullptr), KQ_ERR_NULL);
+  EXPECT(kq_mx_gemm_workspace_size(8, 8, 48, &bytes), KQ_ERR_SHAPE);
+  EXPECT(kq_mx_gemm_workspace_size(-1, 8, 128, &bytes), KQ_ERR_SHAPE);
+  EXPECT(kq_mx_gemm_workspace_size(0, 8, 128, &bytes), KQ_OK);
+  EXPECT((int)bytes, 0);
 
   // expansion, status text
   EXPECT(kq_expand_factors(P, 4, 0, Y, nullptr), KQ_ERR_FORMAT);

@@ -29,7 +29,8 @@ def test_header_symbols_exported(L):
     assert {"kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
             "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug", "hq_quantize",
             "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug", "kq_mx_gemm",
-            "kq_status_string", "kq_last_hip_error"} <= set(names)
+            "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws", "kq_status_string",
+            "kq_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -175,6 +176,28 @@ def test_mx_gemm_validation(L):
     assert g(lda=72) == ALIGN
     assert g(out=X + 2) == ALIGN                 # fp32 output needs 4 bytes
     assert g(M=0, qa=None, sa=None, qb=None, sb=None, out=None) == OK
+    assert g(lda=1 << 24) == SHAPE               # a tile's rows read through one 32-bit range
+    assert g(ldb=1 << 24) == SHAPE
+
+
+def test_mx_gemm_workspace_validation(L):
+    W = 0x60000
+
+    def g(ws=W, nbytes=1 << 20, **kw):
+        a = dict(qa=Q, lda=64, sa=S, ldsa=4, qb=T, ldb=64, sb=Y, ldsb=4, M=8, N=8, K=128, out=X, ldo=8, dt=1)
+        a.update(kw)
+        return L.kq_mx_gemm_ws(a["qa"], a["lda"], a["sa"], a["ldsa"], a["qb"], a["ldb"], a["sb"], a["ldsb"],
+                               a["M"], a["N"], a["K"], a["out"], a["ldo"], a["dt"], ws, nbytes, None)
+    assert g(K=48, lda=32, ldb=32) == SHAPE      # the product's own checks come first
+    assert g(qa=None) == NULL
+    assert g(ws=None, nbytes=4096) == NULL       # a size without a workspace
+    assert g(ws=W + 128) == ALIGN                # 256-byte alignment
+    assert g(M=0, ws=None, nbytes=0, qa=None, sa=None, qb=None, sb=None, out=None) == OK
+    n = ctypes.c_int64(-1)
+    assert L.kq_mx_gemm_workspace_size(8, 8, 128, None) == NULL
+    assert L.kq_mx_gemm_workspace_size(8, 8, 48, ctypes.byref(n)) == SHAPE
+    assert L.kq_mx_gemm_workspace_size(-1, 8, 128, ctypes.byref(n)) == SHAPE
+    assert L.kq_mx_gemm_workspace_size(0, 8, 128, ctypes.byref(n)) == OK and n.value == 0
 
 
 def test_expand_validation(L):

@@ -256,6 +256,22 @@ int kq_mx_gemm_ws(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t lds
                   int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* workspace,
                   int64_t workspace_bytes, void* stream);
 
+/* kq_mx_gemm_ws without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid allocation): same arguments, result and errors as kq_mx_gemm, and it
+ * allocates nothing.  The split tiles meet through the library's own static
+ * device array of 4096 + 128 x 256 KiB bytes (32 MiB + 4 KiB), which every device
+ * the library runs on holds until the process ends; a shape that would need more
+ * (more than 128 split tiles, only on devices of more than 256 compute units)
+ * returns KQ_ERR_VALUE.  The array's address is looked up on a device's first
+ * call, which also clears its flag words with a kernel on `stream`.  Every call on
+ * one device shares that device's array: calls that overlap on one device (other
+ * streams, other threads) race and must not be made.
+ * Errors: as kq_mx_gemm, and KQ_ERR_VALUE. */
+int kq_mx_gemm_static(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
+                      const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+                      int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream);
+
 /* Static text for a kq_status value (never NULL). */
 const char* kq_status_string(int status);
 

@@ -352,6 +352,30 @@ int kq_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes) {
   return KQ_OK;
 }
 
+int kq_mx_gemm_static(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
+                      const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+                      int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream) {
+  bool empty = false;
+  int rc = check_mx_gemm(qa, lda, sa, ldsa, qb, ldb, sb, ldsb, M, N, K, out, ldo, out_dtype, &empty);
+  if (rc != KQ_OK || empty) return rc;
+  int cus = 0;
+  rc = current_cus(&cus);
+  if (rc != KQ_OK) return rc;
+  const int64_t need = kq::mx_gemm_workspace_bytes(M, N, K, cus);
+  if (need > kq::kStaticScratchBytes) return KQ_ERR_VALUE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = kq::static_scratch(&ws, stream);
+    if (e != hipSuccess) return fail_hip(e);
+  }
+  kq::GemmArgs g{qa, lda, sa, ldsa, qb, ldb, sb, ldsb, M, N, K, out, ldo,
+                 out_dtype == KQ_BF16, stream, cus};
+  g.workspace = ws;
+  g.workspace_bytes = ws ? kq::kStaticScratchBytes : 0;
+  const hipError_t e = kq::launch_mx_gemm(g);
+  return e == hipSuccess ? KQ_OK : fail_hip(e);
+}
+
 int kq_mx_gemm_ws(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
                   const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
                   int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* workspace,

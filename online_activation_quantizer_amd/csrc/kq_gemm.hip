@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "kq_launch.hpp"
@@ -557,7 +558,42 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   else write_tile(h_tile, stored_sums);
 }
 
+// The static split workspace (kq_mx_gemm_static): zero-initialized with the
+// code object; its flags are cleared once more on each device's first use.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+__global__ __launch_bounds__(256) void clear_flags_kernel(uint32_t* __restrict__ flags, uint32_t n) {
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) flags[i] = 0u;
+}
+
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+
 }  // namespace
+
+hipError_t static_scratch(void** ptr, void* stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [&] {
+    // the array's device address on this device (in host code its name is only a
+    // stand-in); every later use goes through this pointer
+    void* p = nullptr;
+    hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r == hipSuccess) {
+      hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream,
+                         static_cast<uint32_t*>(p), (uint32_t)(kSplitFlagBytes / 4));
+      r = hipGetLastError();
+    }
+    g_scratch_ptr[dev] = r == hipSuccess ? p : nullptr;
+    g_scratch_err[dev] = r;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
 
 // The grid and the tiles' order for one product (the kernel's unit list).
 struct Schedule {

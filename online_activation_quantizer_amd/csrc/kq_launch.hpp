@@ -69,6 +69,16 @@ constexpr int64_t kSplitFlagBytes = 4096;
 constexpr int64_t kSplitMaxTiles = kSplitFlagBytes / 4;
 constexpr int64_t kSplitTileBytes = 256 * 256 * 4;
 
+// The library's own split workspace for callers that cannot allocate: a static
+// device array of kStaticScratchBytes on every device the library runs on (flags,
+// then the partial sums of up to kStaticSplitTiles tiles, the most a device of 256
+// compute units splits).
+constexpr int64_t kStaticSplitTiles = 128;
+constexpr int64_t kStaticScratchBytes = kSplitFlagBytes + kStaticSplitTiles * kSplitTileBytes;
+// Device address of the current device's static workspace (set up on its first
+// use: looked up once, flags cleared by a kernel on `stream`).
+hipError_t static_scratch(void** ptr, void* stream);
+
 inline int64_t gcd64(int64_t a, int64_t b) {
   while (b) {
     const int64_t r = a % b;

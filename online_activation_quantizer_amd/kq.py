@@ -33,8 +33,8 @@ KQ_AUTO, KQ_BUTTERFLY, KQ_MFMA = 0, 1, 2
 EXPORTED_SYMBOLS = ("kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
                     "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug",
                     "hq_quantize", "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug",
-                    "kq_mx_gemm", "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws", "kq_status_string",
-                    "kq_last_hip_error")
+                    "kq_mx_gemm", "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws", "kq_mx_gemm_static",
+                    "kq_status_string", "kq_last_hip_error")
 
 
 class KQError(RuntimeError):
@@ -72,6 +72,7 @@ def lib():
         L.kq_mx_gemm.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, I64, I, P]
         L.kq_mx_gemm_workspace_size.argtypes = [I64, I64, I64, ctypes.POINTER(I64)]
         L.kq_mx_gemm_ws.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, I64, I, P, I64, P]
+        L.kq_mx_gemm_static.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, I64, I, P]
         L.kq_status_string.argtypes = [I]
         L.kq_status_string.restype = ctypes.c_char_p
         L.kq_last_hip_error.argtypes = []
@@ -410,9 +411,10 @@ def _mx_gemm(what, qa, sa, qb, sb, out, out_dtype, workspace, stream):
     _row_pitch(out)
     args = (qa.data_ptr(), _row_pitch(qa), sa.data_ptr(), _row_pitch(sa), qb.data_ptr(), _row_pitch(qb),
             sb.data_ptr(), _row_pitch(sb), M, N, K, out.data_ptr(), _row_pitch(out), code)
-    if workspace is False:
+    if workspace is False or workspace == "static":
         _need_device(what, qa, sa=sa, qb=qb, sb=sb, out=out)
-        _check(lib().kq_mx_gemm(*args, _stream(stream)), what)
+        fn = lib().kq_mx_gemm if workspace is False else lib().kq_mx_gemm_static
+        _check(fn(*args, _stream(stream)), what)
         return out
     if workspace is None:
         _need_device(what, qa, sa=sa, qb=qb, sb=sb, out=out)
@@ -429,6 +431,13 @@ def kq_mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
     """W4A4 product out[m][n] = sum_k deq(A)[m][k] deq(B)[n][k] of two MXFP4 operands
     (codes [rows, K/2], scales [rows, K/32]); out float32 (default) or bfloat16."""
     return _mx_gemm("kq_mx_gemm", qa, sa, qb, sb, out, out_dtype, False, stream)
+
+
+def kq_mx_gemm_static(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
+    """kq_mx_gemm_ws through the library's static device workspace: allocates
+    nothing (beyond ``out`` when it is not given).  Calls that overlap on one device
+    race."""
+    return _mx_gemm("kq_mx_gemm_static", qa, sa, qb, sb, out, out_dtype, "static", stream)
 
 
 def kq_mx_gemm_workspace_size(M: int, N: int, K: int) -> int:

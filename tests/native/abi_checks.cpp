@@ -120,6 +120,14 @@ int main() {
   EXPECT(kq_mx_gemm_ws(nullptr, 64, nullptr, 4, nullptr, 64, nullptr, 4, 8, 0, 128, nullptr, 8, 1, W, 0,
                        nullptr),
          KQ_OK);
+  // the static-workspace variant: the product's checks, before any HIP call
+  EXPECT(kq_mx_gemm_static(Q, 64, S, 4, T, 64, S, 4, 8, 8, 128, X, 8, 5, nullptr), KQ_ERR_DTYPE);
+  EXPECT(kq_mx_gemm_static(Q, 64, S, 4, T, 64, S, 4, 8, 8, 48, X, 8, 1, nullptr), KQ_ERR_SHAPE);
+  EXPECT(kq_mx_gemm_static(nullptr, 64, S, 4, T, 64, S, 4, 8, 8, 128, X, 8, 1, nullptr), KQ_ERR_NULL);
+  EXPECT(kq_mx_gemm_static(Q + 8, 64, S, 4, T, 64, S, 4, 8, 8, 128, X, 8, 1, nullptr), KQ_ERR_ALIGN);
+  EXPECT(kq_mx_gemm_static(nullptr, 64, nullptr, 4, nullptr, 64, nullptr, 4, 0, 8, 128, nullptr, 8, 1,
+                           nullptr),
+         KQ_OK);
   int64_t bytes = -1;
   EXPECT(kq_mx_gemm_workspace_size(8, 8, 128, nullptr), KQ_ERR_NULL);
   EXPECT(kq_mx_gemm_workspace_size(8, 8, 48, &bytes), KQ_ERR_SHAPE);

@@ -29,7 +29,7 @@ def test_header_symbols_exported(L):
     assert {"kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
             "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug", "hq_quantize",
             "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug", "kq_mx_gemm",
-            "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws", "kq_status_string",
+            "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws", "kq_mx_gemm_static", "kq_status_string",
             "kq_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -193,6 +193,16 @@ def test_mx_gemm_workspace_validation(L):
     assert g(ws=None, nbytes=4096) == NULL       # a size without a workspace
     assert g(ws=W + 128) == ALIGN                # 256-byte alignment
     assert g(M=0, ws=None, nbytes=0, qa=None, sa=None, qb=None, sb=None, out=None) == OK
+    def st(**kw):
+        a = dict(qa=Q, lda=64, sa=S, ldsa=4, qb=T, ldb=64, sb=Y, ldsb=4, M=8, N=8, K=128, out=X, ldo=8, dt=1)
+        a.update(kw)
+        return L.kq_mx_gemm_static(a["qa"], a["lda"], a["sa"], a["ldsa"], a["qb"], a["ldb"], a["sb"],
+                                   a["ldsb"], a["M"], a["N"], a["K"], a["out"], a["ldo"], a["dt"], None)
+    assert st(dt=5) == DTYPE                     # the static-workspace variant: the product's checks
+    assert st(K=48, lda=32, ldb=32) == SHAPE
+    assert st(qb=None) == NULL
+    assert st(out=X + 2) == ALIGN
+    assert st(M=0, qa=None, sa=None, qb=None, sb=None, out=None) == OK
     n = ctypes.c_int64(-1)
     assert L.kq_mx_gemm_workspace_size(8, 8, 128, None) == NULL
     assert L.kq_mx_gemm_workspace_size(8, 8, 48, ctypes.byref(n)) == SHAPE

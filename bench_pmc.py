@@ -131,7 +131,9 @@ TRACE_KERNELS = [
     ("void kq::(anonymous namespace)::norm_kernel<0, true, false>", "`norm_kernel<bf16, modulated>` (kq_norm_quantize)"),
     ("void kq::(anonymous namespace)::butterfly_kernel<0, false, 1>",
      "`butterfly_kernel<bf16, -, weights>` (kq_quantize_weights, 12288x3072)"),
-    ("void kq::(anonymous namespace)::mx_gemm_kernel<", "`mx_gemm_kernel<256x256 tiles, bf16 out, staged>` (kq_mx_gemm, 4608x12288x3072)"),
+    ("gemm unsplit 216", "`mx_gemm_kernel<256x256 tiles, bf16 out, staged>` (kq_mx_gemm, 4608x12288x3072, 216 workgroups)"),
+    ("gemm unsplit 48", "`mx_gemm_kernel<256x256 tiles, bf16 out, staged>` (kq_mx_gemm, 1024x3072x12288, 48 workgroups)"),
+    ("gemm split 96", "`mx_gemm_kernel<..., split>` (kq_mx_gemm_ws, 1024x3072x12288 in K halves, 96 workgroups)"),
     ("mlp-shape void kq::(anonymous namespace)::butterfly_kernel<0, false, 0>",
      "`butterfly_kernel<bf16, -, forward>` on 4608x12288 (the last leg)"),
     ("void at::native::(anonymous namespace)::vectorized_layer_norm_kernel", "torch layer_norm (unfused sequence)"),
@@ -155,6 +157,11 @@ def trace(trace_dir, bench_json):
         name = r["Kernel_Name"]
         if name.startswith(fwd) and gemm_end is not None and int(r["Start_Timestamp"]) > gemm_end:
             name = "mlp-shape " + name
+        if "mx_gemm_kernel<" in name:
+            # one row per product: the split variant's last template argument is true;
+            # the grid (workgroups of 512 lanes) tells the two unsplit shapes apart
+            grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0) // 512
+            name = f"gemm {'split' if name.split('>(')[0].endswith('true') else 'unsplit'} {grid}"
         dur.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
     b = json.load(open(bench_json))
 

@@ -566,6 +566,44 @@ def gemm_split_timing(args):
             "rel_diff_vs_unsplit": round(rel, 6)}
 
 
+def gemm_fused_timing(args):
+    """The product with the quantizer in its prologue (kq_mx_gemm_fused: bf16 X and
+    the factor parameters in, no MXFP4 activation operand in memory) beside the
+    unfused pair (kq_quantize, then kq_mx_gemm, in one graph) on the FLUX.1-schnell
+    MLP up-projection, and on its first 256 weight rows (one tile column of Y, the
+    case where the fused path quantizes each activation tile only once)."""
+    import torch
+
+    import synth
+    import online_activation_quantizer_amd as kq
+    cfg, wcfg = synth.get_config("flux"), synth.get_weight_config("flux_w_mlp")
+    x, p, _ = synth.make_inputs(cfg)
+    w, pw = synth.make_weights(wcfg)
+    xd, pd = torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(p).cuda()
+    qw, sw = kq.kq_quantize_weights(torch.from_numpy(w.view(np.int16)).cuda(), torch.from_numpy(pw).cuda())
+    M, K = xd.shape
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+    steps = max(8, args.steps // 10)
+    res = {"workload": f"FLUX.1-schnell MLP up-projection from bf16 activations, {M}x{wcfg.rows}x{K} and "
+                       f"{M}x256x{K}, bf16 out"}
+    for N in (wcfg.rows, 256):
+        qb, sb = qw[:N], sw[:N]
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        legs = {}
+        for name, fn in (("fused", lambda i: kq.kq_mx_gemm_fused(xd, pd, qb, sb, out=out)),
+                         ("quantize_then_product", lambda i: (kq.kq_quantize(xd, pd, q=q, s=s),
+                                                              kq.kq_mx_gemm(q, s, qb, sb, out=out)))):
+            ms = (timed(fn, steps, args.warmup, torch.cuda.current_stream()) if args.eager
+                  else timed_graph(fn, steps, min(args.warmup, 10)))
+            legs[name] = {"ms_per_call": round(ms, 6),
+                          "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+        legs["t_fused_over_t_unfused"] = round(legs["fused"]["ms_per_call"] /
+                                               legs["quantize_then_product"]["ms_per_call"], 4)
+        res[f"n{N}"] = legs
+    return res
+
+
 def library_gemm_timing(args, qs, ss, qw, sw, ours):
     """The same MXFP4 x MXFP4 product through torch's scaled matmul (the vendor BLAS
     path; block-scaled products come out in bf16 only), timed the same way, with its
@@ -754,6 +792,7 @@ def main():
     gemm = None if args.no_gemm else gemm_timing(args, qs, ss)
     if gemm is not None:
         gemm["few_tiles_split"] = gemm_split_timing(args)
+        gemm["prologue_fused"] = gemm_fused_timing(args)
     mlp = None if args.no_mlp else mlp_timing(args)
     shard = None if args.no_shard or args.variant != "butterfly" else shard_timing(args, xs, ps)
     sweep = None if args.no_sweep else sweep_timing(args)

@@ -229,6 +229,23 @@ int kq_mx_gemm(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
                const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
                int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream);
 
+/* The W4A4 product with the quantizer in its prologue (KroQuant abstract: the
+ * online transform feeds the W4A4 MXFP4 product):
+ *   out[m][n] = sum_k deq(Q(T X))[m][k] * deq(B)[n][k]
+ * X: bf16 [M][ldx] activations (dtype KQ_BF16; KQ_FP32 returns KQ_ERR_DTYPE),
+ * ldx >= K elements, x and its row pitch 16-byte aligned; params: fp32
+ * [K/32][5][3] factor parameters (l, u, v) as kq_quantize takes them (KQ_T_PARAMS);
+ * B: the weights as kq_quantize_weights writes them (qb [N][ldb], sb [N][ldsb]); out
+ * as kq_mx_gemm.  The activations' codes and scales are those kq_quantize computes,
+ * bit for bit, and the product is kq_mx_gemm's: the result equals kq_mx_gemm on
+ * kq_quantize's output exactly.  K: multiple of 32, at most 16384 (every block's
+ * transform constants are held on chip).  The activation tile is quantized again
+ * for every 256-column tile of out, so this pays only when N is small.
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_DTYPE, KQ_ERR_HIP. */
+int kq_mx_gemm_fused(const void* x, int dtype, int64_t ldx, const float* params,
+                     const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+                     int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream);
+
 /* Bytes of device workspace that kq_mx_gemm_ws uses for an M x N x K product on
  * the current device (written to *bytes; 0 when nothing is split, which is then
  * the same product as kq_mx_gemm).  The product computes 256 x 256 output tiles, at

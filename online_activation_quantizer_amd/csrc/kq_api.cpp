@@ -338,6 +338,29 @@ int kq_mx_gemm(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
                       0, stream);
 }
 
+int kq_mx_gemm_fused(const void* x, int dtype, int64_t ldx, const float* params,
+                     const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+                     int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream) {
+  if (dtype != KQ_BF16) return KQ_ERR_DTYPE;  // the prologue reads bf16 activations only
+  if (out_dtype != KQ_FP32 && out_dtype != KQ_BF16) return KQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || K / 32 > kq::kFusedMaxBlocks || M > kMaxRows ||
+      N > kMaxRows || ldx < K || ldb < K / 2 || ldsb < K / 32 || ldo < N || ldx * 2 > kMaxPitch ||
+      ldb > kMaxPitch || ldsb > kMaxPitch || ldo * (out_dtype == KQ_FP32 ? 4 : 2) > kMaxPitch)
+    return KQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return KQ_OK;
+  if (!x || !params || !qb || !sb || !out) return KQ_ERR_NULL;
+  if (!aligned(x, 16) || (ldx * 2) % 16 != 0 || !aligned(qb, 16) || ldb % 16 != 0 ||
+      !aligned(out, out_dtype == KQ_FP32 ? 4 : 2))
+    return KQ_ERR_ALIGN;
+  int cus = 0;
+  const int rc = current_cus(&cus);
+  if (rc != KQ_OK) return rc;
+  const kq::FusedGemmArgs g{x, ldx, params, qb, ldb, sb, ldsb, M, N, K, out, ldo,
+                            out_dtype == KQ_BF16, stream, cus};
+  const hipError_t e = kq::launch_mx_gemm_fused(g);
+  return e == hipSuccess ? KQ_OK : fail_hip(e);
+}
+
 int kq_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes) {
   if (!bytes) return KQ_ERR_NULL;
   *bytes = 0;

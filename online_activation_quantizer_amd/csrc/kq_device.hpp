@@ -109,14 +109,13 @@ __device__ __forceinline__ uint32_t e8m0_of_amax(float m) {
   return E >= 255u ? 255u : (E > 2u ? E - 2u : 0u);
 }
 
-// Encode 32 fp32 values as MXFP4 and store 16 code bytes + 1 scale byte.
-// The hardware scaled convert divides by 2^(exponent field of its scale
-// operand), rounds to nearest even, saturates at 6 and keeps the sign of zero.
-// Blocks whose scale is tiny (byte < 25) are pre-multiplied by 2^64 (exact:
-// their amax is below 2^-100) so that the convert never sees a subnormal
-// scale or subnormal inputs.
-__device__ __forceinline__ void encode_store(float (&y)[kBlk], uint8_t* __restrict__ qp,
-                                             uint8_t* __restrict__ sp) {
+// Encode 32 fp32 values as MXFP4: 16 code bytes into w (low nibble first) and
+// the E8M0 scale byte as the result.  The hardware scaled convert divides by
+// 2^(exponent field of its scale operand), rounds to nearest even, saturates at 6
+// and keeps the sign of zero.  Blocks whose scale is tiny (byte < 25) are
+// pre-multiplied by 2^64 (exact: their amax is below 2^-100) so that the convert
+// never sees a subnormal scale or subnormal inputs.
+__device__ __forceinline__ uint32_t encode(float (&y)[kBlk], uint32_t (&w)[4]) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < kBlk; i += 2) m = amax3(m, y[i], y[i + 1]);
@@ -128,7 +127,6 @@ __device__ __forceinline__ void encode_store(float (&y)[kBlk], uint8_t* __restri
     Sc = S + 64u;
   }
   const float sc = __uint_as_float(Sc << 23);
-  uint32_t w[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     uint32_t a = 0;
@@ -138,6 +136,14 @@ __device__ __forceinline__ void encode_store(float (&y)[kBlk], uint8_t* __restri
     a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, y[8 * k + 6], y[8 * k + 7], sc, 3);
     w[k] = S == 255u ? 0u : a;
   }
+  return S;
+}
+
+// encode, then store the 16 code bytes at qp and the scale byte at sp.
+__device__ __forceinline__ void encode_store(float (&y)[kBlk], uint8_t* __restrict__ qp,
+                                             uint8_t* __restrict__ sp) {
+  uint32_t w[4];
+  const uint32_t S = encode(y, w);
   // streaming stores: the codes are consumed by a later kernel, not re-read here
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 wv = {w[0], w[1], w[2], w[3]};

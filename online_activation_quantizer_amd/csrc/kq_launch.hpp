@@ -79,6 +79,26 @@ constexpr int64_t kStaticScratchBytes = kSplitFlagBytes + kStaticSplitTiles * kS
 // use: looked up once, flags cleared by a kernel on `stream`).
 hipError_t static_scratch(void** ptr, void* stream);
 
+// The W4A4 product with the quantizer in its prologue: X bf16 [M][ldx] and its
+// factor parameters [K/32][15] in place of the activations' MXFP4 operand.
+struct FusedGemmArgs {
+  const void* x;
+  int64_t ldx;  // elements
+  const float* params;
+  const uint8_t* qb;
+  int64_t ldb;  // bytes
+  const uint8_t* sb;
+  int64_t ldsb;
+  int64_t M, N, K;
+  void* out;    // [M][ldo] float32 or bf16
+  int64_t ldo;  // elements
+  bool out_bf16;
+  void* stream;
+  int cus;
+};
+// Every block's transform constants sit in the fused product's LDS: K <= 32 x this.
+constexpr int64_t kFusedMaxBlocks = 512;
+
 inline int64_t gcd64(int64_t a, int64_t b) {
   while (b) {
     const int64_t r = a % b;
@@ -109,6 +129,7 @@ hipError_t launch_weights(const LaunchArgs& a);   // W T^-1 along each row, then
 hipError_t launch_hadamard(const LaunchArgs& a);  // fixed block-Hadamard, then MXFP4
 hipError_t launch_norm(const NormArgs& n);        // LayerNorm + modulation, T_b, MXFP4
 hipError_t launch_mx_gemm(const GemmArgs& g);    // Y = deq(A) deq(B)^T on scaled MFMA
+hipError_t launch_mx_gemm_fused(const FusedGemmArgs& g);  // Y = deq(Q(T X)) deq(B)^T
 // bytes of workspace the product's split tiles need (0: nothing is split)
 int64_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_sq(const LaunchArgs& a);

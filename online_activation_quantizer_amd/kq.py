@@ -33,7 +33,8 @@ KQ_AUTO, KQ_BUTTERFLY, KQ_MFMA = 0, 1, 2
 EXPORTED_SYMBOLS = ("kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
                     "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug",
                     "hq_quantize", "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug",
-                    "kq_mx_gemm", "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws", "kq_mx_gemm_static",
+                    "kq_mx_gemm", "kq_mx_gemm_fused", "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws",
+                    "kq_mx_gemm_static",
                     "kq_status_string", "kq_last_hip_error")
 
 
@@ -73,6 +74,7 @@ def lib():
         L.kq_mx_gemm_workspace_size.argtypes = [I64, I64, I64, ctypes.POINTER(I64)]
         L.kq_mx_gemm_ws.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, I64, I, P, I64, P]
         L.kq_mx_gemm_static.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, I64, I, P]
+        L.kq_mx_gemm_fused.argtypes = [P, I, I64, P, P, I64, P, I64, I64, I64, I64, P, I64, I, P]
         L.kq_status_string.argtypes = [I]
         L.kq_status_string.restype = ctypes.c_char_p
         L.kq_last_hip_error.argtypes = []
@@ -431,6 +433,44 @@ def kq_mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
     """W4A4 product out[m][n] = sum_k deq(A)[m][k] deq(B)[n][k] of two MXFP4 operands
     (codes [rows, K/2], scales [rows, K/32]); out float32 (default) or bfloat16."""
     return _mx_gemm("kq_mx_gemm", qa, sa, qb, sb, out, out_dtype, False, stream)
+
+
+def kq_mx_gemm_fused(x, params, qb, sb, out=None, out_dtype=None, stream=None):
+    """The W4A4 product with the quantizer in its prologue: out = deq(Q(T x))
+    deq(B)^T from bf16 x [M, K], its float32 factor parameters [K/32, 5, 3] and the
+    weights' MXFP4 operand (codes [N, K/2], scales [N, K/32]); equal to
+    kq_mx_gemm(*kq_quantize(x, params), qb, sb) bit for bit."""
+    import torch
+    what = "kq_mx_gemm_fused"
+    _need_input(what, x)
+    if _dtype_code(x) != KQ_BF16:
+        _fail(KQ_ERR_DTYPE, f"{what}: x must be bf16, got {x.dtype}")
+    M, K = x.shape
+    if K % 32 != 0:
+        _fail(KQ_ERR_SHAPE, f"{what}: K = {K} is not a multiple of 32")
+    _need_flat(what, "params", params, K // 32 * 15, _f32, "float32 [K/32, 5, 3]")
+    for name, t in (("qb", qb), ("sb", sb)):
+        if t.dim() != 2:
+            _fail(KQ_ERR_SHAPE, f"{what}: {name} must be 2-D, got {tuple(t.shape)}")
+        if t.dtype != torch.uint8:
+            _fail(KQ_ERR_DTYPE, f"{what}: {name} must be uint8, got {t.dtype}")
+        _row_pitch(t)
+    N = qb.shape[0]
+    if qb.shape[1] != K // 2 or tuple(sb.shape) != (N, K // 32):
+        _fail(KQ_ERR_SHAPE, f"{what}: weights need codes [N, K/2] and scales [N, K/32] for K = {K}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=x.device)
+    code = {torch.float32: KQ_FP32, torch.bfloat16: KQ_BF16}.get(out.dtype)
+    if code is None:
+        _fail(KQ_ERR_DTYPE, f"unsupported output dtype {out.dtype}")
+    if out.dim() != 2 or tuple(out.shape) != (M, N):
+        _fail(KQ_ERR_SHAPE, f"{what}: out is {tuple(out.shape)}, needs ({M}, {N})")
+    _row_pitch(out)
+    _need_device(what, x, params=params, qb=qb, sb=sb, out=out)
+    _check(lib().kq_mx_gemm_fused(x.data_ptr(), KQ_BF16, _row_pitch(x), params.data_ptr(), qb.data_ptr(),
+                                  _row_pitch(qb), sb.data_ptr(), _row_pitch(sb), M, N, K, out.data_ptr(),
+                                  _row_pitch(out), code, _stream(stream)), what)
+    return out
 
 
 def kq_mx_gemm_static(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):

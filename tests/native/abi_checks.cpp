@@ -128,6 +128,14 @@ int main() {
   EXPECT(kq_mx_gemm_static(nullptr, 64, nullptr, 4, nullptr, 64, nullptr, 4, 0, 8, 128, nullptr, 8, 1,
                            nullptr),
          KQ_OK);
+  // the prologue-fused product: bf16 activations, K <= 16384
+  EXPECT(kq_mx_gemm_fused(X, 1, 128, P, Q, 64, S, 4, 8, 8, 128, Y, 8, 1, nullptr), KQ_ERR_DTYPE);
+  EXPECT(kq_mx_gemm_fused(X, 0, 16416, P, Q, 8208, S, 513, 8, 8, 16416, Y, 8, 1, nullptr), KQ_ERR_SHAPE);
+  EXPECT(kq_mx_gemm_fused(X, 0, 128, nullptr, Q, 64, S, 4, 8, 8, 128, Y, 8, 1, nullptr), KQ_ERR_NULL);
+  EXPECT(kq_mx_gemm_fused(X + 8, 0, 128, P, Q, 64, S, 4, 8, 8, 128, Y, 8, 1, nullptr), KQ_ERR_ALIGN);
+  EXPECT(kq_mx_gemm_fused(nullptr, 0, 128, nullptr, nullptr, 64, nullptr, 4, 0, 8, 128, nullptr, 8, 1,
+                          nullptr),
+         KQ_OK);
   int64_t bytes = -1;
   EXPECT(kq_mx_gemm_workspace_size(8, 8, 128, nullptr), KQ_ERR_NULL);
   EXPECT(kq_mx_gemm_workspace_size(8, 8, 48, &bytes), KQ_ERR_SHAPE);

@@ -29,7 +29,8 @@ def test_header_symbols_exported(L):
     assert {"kq_expand_factors", "kq_quantize", "sq_quantize", "kq_transform_debug",
             "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug", "hq_quantize",
             "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug", "kq_mx_gemm",
-            "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws", "kq_mx_gemm_static", "kq_status_string",
+            "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws", "kq_mx_gemm_static", "kq_mx_gemm_fused",
+            "kq_status_string",
             "kq_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -178,6 +179,22 @@ def test_mx_gemm_validation(L):
     assert g(M=0, qa=None, sa=None, qb=None, sb=None, out=None) == OK
     assert g(lda=1 << 24) == SHAPE               # a tile's rows read through one 32-bit range
     assert g(ldb=1 << 24) == SHAPE
+
+
+def test_mx_gemm_fused_validation(L):
+    def g(x=X, dt=0, ldx=128, p=T, qb=Q, ldb=64, sb=S, ldsb=4, M=8, N=8, K=128, out=Y, ldo=8, odt=1):
+        return L.kq_mx_gemm_fused(x, dt, ldx, p, qb, ldb, sb, ldsb, M, N, K, out, ldo, odt, None)
+    assert g(dt=1) == DTYPE                      # fp32 activations: the prologue reads bf16
+    assert g(odt=7) == DTYPE
+    assert g(K=48, ldb=32) == SHAPE              # K not a multiple of 32
+    assert g(K=16416, ldx=16416, ldb=8208, ldsb=513) == SHAPE  # 513 blocks: past the on-chip constants
+    assert g(ldx=64) == SHAPE                    # row pitch below K
+    assert g(ldsb=3) == SHAPE
+    assert g(p=None) == NULL
+    assert g(x=None) == NULL
+    assert g(x=X + 8) == ALIGN
+    assert g(ldx=132) == ALIGN                   # 264-byte rows
+    assert g(M=0, x=None, p=None, qb=None, sb=None, out=None) == OK
 
 
 def test_mx_gemm_workspace_validation(L):

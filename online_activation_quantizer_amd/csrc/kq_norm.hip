@@ -246,6 +246,202 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void n
   }
 }
 
+// Half wave per row (bf16 rows of at most 32 KB blocks, KB <= 4: d <= 4096).  Each
+// half wave of 32 lanes takes one row, lane l the blocks l, l + 32, ... (KB of them,
+// past nb idle), so both reductions of a row are 5 lane exchanges and a read of one
+// lane, with no LDS and no barrier; a workgroup of 4 waves holds 8 rows.  The
+// per-block constants (the diagonal times 1 + scale, the shear coefficients and
+// c = T_b shift) are built once per workgroup and sample into LDS, at the top of
+// the sample's first pass, and every lane reads its blocks' from there: 42 + 32
+// constants per block cost no registers between rows.  At d = 3072 the kernel needs
+// 165 VGPRs, three waves per SIMD (4608 x 3072: 14.6 -> 13.8 us against the LDS
+// meeting of half waves).  Building the constants while the rows are in flight
+// keeps more registers live than three waves per SIMD allow (185-215 VGPRs,
+// 14.6-17.1 us, in every order tried), and widening the rows again in each pass to
+// reach four waves per SIMD (124 VGPRs) costs more VALU than it hides (15.3 us).
+constexpr int kHwRows = 8;                 // rows per workgroup pass (one per half wave)
+constexpr int kHwMaxBlocks = 128;          // d <= 4096
+constexpr int kHwStride = 76;              // floats per block in LDS: e[32] su[5] ll[5] . . c[32] . .
+
+template <bool MOD, bool WRITE_Y, int KB>
+__global__ __launch_bounds__(256) void norm_hw_kernel(
+    const uint8_t* __restrict__ x, uint32_t rows, uint32_t nb, uint32_t ldx,
+    const float* __restrict__ shift, const float* __restrict__ scale, uint32_t rows_per_sample,
+    float eps, float inv_d, const float* __restrict__ params, uint8_t* __restrict__ q,
+    uint32_t ldq, uint8_t* __restrict__ s, uint32_t lds, float* __restrict__ y, uint32_t ldy) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) float cs[kHwMaxBlocks * kHwStride];
+  const uint32_t hw = threadIdx.x >> 5, l = threadIdx.x & 31u;
+  const uint32_t last = rows - 1;
+  const uint64_t d = (uint64_t)nb * kBlk;
+  // the sample whose constants are in LDS (none yet)
+  uint64_t cur_g = ~0ull;
+  // the constants of sample g for every block, by the workgroup's lanes
+  auto build = [&](uint64_t g) {
+    for (uint32_t b = threadIdx.x; b < nb; b += blockDim.x) {
+      BlockParams bp = load_params(params, b);
+      BlockConsts k;
+      make_consts<false>(bp, k);
+      float* dst = cs + b * kHwStride;
+      if (MOD) {
+        float cv[kBlk];
+        const f32x4* o4 = reinterpret_cast<const f32x4*>(shift + g * d + (uint64_t)b * kBlk);
+#pragma unroll
+        for (int j = 0; j < kBlk / 4; ++j) {
+          const f32x4 o = o4[j];
+          cv[4 * j] = o.x;
+          cv[4 * j + 1] = o.y;
+          cv[4 * j + 2] = o.z;
+          cv[4 * j + 3] = o.w;
+        }
+        transform<false>(cv, k);  // c = T_b shift, with the unmodulated diagonal
+        const f32x4* a4 = reinterpret_cast<const f32x4*>(scale + g * d + (uint64_t)b * kBlk);
+#pragma unroll
+        for (int j = 0; j < kBlk / 4; ++j) {
+          const f32x4 a = a4[j];
+          k.d[4 * j] *= 1.0f + a.x;
+          k.d[4 * j + 1] *= 1.0f + a.y;
+          k.d[4 * j + 2] *= 1.0f + a.z;
+          k.d[4 * j + 3] *= 1.0f + a.w;
+        }
+#pragma unroll
+        for (int i = 0; i < kBlk; ++i) dst[44 + i] = cv[i];
+      }
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) dst[i] = k.d[i];
+#pragma unroll
+      for (int j = 0; j < 5; ++j) {
+        dst[kBlk + j] = k.su[j];
+        dst[kBlk + 5 + j] = k.ll[j];
+      }
+    }
+    cur_g = g;
+  };
+
+  // Passes of up to 8 rows of one sample: pass i is chunk i % chunks of sample
+  // i / chunks (chunks = ceil(rows_per_sample / 8); without modulation, one sample
+  // of all rows), so a sample's constants are built once per workgroup and
+  // sample, at the top of its first pass.
+  const uint32_t rps = MOD && rows_per_sample < rows ? rows_per_sample : rows;
+  const uint32_t chunks = (rps + kHwRows - 1) / kHwRows;
+  const uint32_t samples = (rows + rps - 1) / rps;
+  const uint64_t passes = (uint64_t)samples * chunks;
+  for (uint64_t pi = blockIdx.x; pi < passes; pi += gridDim.x) {
+    const uint64_t g = pi / chunks;
+    const uint32_t row0 = (uint32_t)(g * rps + (pi % chunks) * kHwRows);
+    const uint64_t send = (g + 1) * rps;
+    const uint32_t rend = send < rows ? (uint32_t)send : rows;  // the pass's rows: [row0, rend)
+    if (g != cur_g) {
+      __syncthreads();  // every wave past its reads of the previous sample's constants
+      build(g);
+      __syncthreads();
+    }
+    // this half wave's row (past the pass: its first row again, not stored) and its
+    // blocks' raw bytes, all requested first
+    const uint32_t r = row0 + hw;
+    const bool row_ok = r < rend;
+    const uint32_t rr = row_ok ? r : row0;
+    Raw<DT_BF16> raw[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const uint32_t j = l + 32u * k, jj = j < nb ? j : nb - 1u;
+      raw[k] = load_raw<DT_BF16>(x + (uint64_t)rr * ldx + (uint64_t)jj * (kBlk * 2));
+    }
+    // the mean: each lane's blocks by pairwise sums, in block order, then the half
+    // wave's 32 lanes
+    float sum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      float v[kBlk];
+      unpack(raw[k], v);
+      const float bs = block_sum(v);
+      sum += l + 32u * k < nb ? bs : 0.0f;
+    }
+    const float mu = half_sum(sum) * inv_d;
+    // the variance: squared deviations from the mean, the same way
+    float m2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      float v[kBlk];
+      unpack(raw[k], v);
+      float bm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) {
+        const float dv = v[i] - mu;
+        bm = __builtin_fmaf(dv, dv, bm);
+      }
+      m2 += l + 32u * k < nb ? bm : 0.0f;
+    }
+    const float rstd = __builtin_amdgcn_rsqf(half_sum(m2) * inv_d + eps);
+    if (!row_ok) continue;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const uint32_t j = l + 32u * k;
+      if (j >= nb) continue;
+      float v[kBlk];
+      unpack(raw[k], v);
+      const f32x4* c4 = reinterpret_cast<const f32x4*>(cs + j * kHwStride);
+#pragma unroll
+      for (int i = 0; i < kBlk / 4; ++i) {
+        const f32x4 e = c4[i];
+        v[4 * i] = (v[4 * i] - mu) * e.x;
+        v[4 * i + 1] = (v[4 * i + 1] - mu) * e.y;
+        v[4 * i + 2] = (v[4 * i + 2] - mu) * e.z;
+        v[4 * i + 3] = (v[4 * i + 3] - mu) * e.w;
+      }
+      BlockConsts k2;
+      const f32x4 sa = c4[8], sbq = c4[9], sc2 = c4[10];
+      const float sh[12] = {sa.x, sa.y, sa.z, sa.w, sbq.x, sbq.y, sbq.z, sbq.w, sc2.x, sc2.y, sc2.z, sc2.w};
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        k2.su[i] = sh[i];
+        k2.ll[i] = sh[5 + i];
+      }
+      shears<false>(v, k2);
+      if (MOD) {
+#pragma unroll
+        for (int i = 0; i < kBlk / 4; ++i) {
+          const f32x4 c = c4[11 + i];
+          v[4 * i] = __builtin_fmaf(rstd, v[4 * i], c.x);
+          v[4 * i + 1] = __builtin_fmaf(rstd, v[4 * i + 1], c.y);
+          v[4 * i + 2] = __builtin_fmaf(rstd, v[4 * i + 2], c.z);
+          v[4 * i + 3] = __builtin_fmaf(rstd, v[4 * i + 3], c.w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kBlk; ++i) v[i] *= rstd;
+      }
+      if (WRITE_Y)
+        store_y(reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(y) + (uint64_t)r * ldy) + j * kBlk, v);
+      encode_store(v, q + (uint64_t)r * ldq + j * (kBlk / 2), s + (uint64_t)r * lds + j);
+    }
+  }
+}
+
+template <bool MOD, bool WRITE_Y, int KB>
+hipError_t launch_hw_t(const NormArgs& n) {
+  const LaunchArgs& a = n.a;
+  const int64_t rps = MOD && n.rows_per_sample < a.rows ? n.rows_per_sample : a.rows;
+  const int64_t groups = (a.rows + rps - 1) / rps * ((rps + kHwRows - 1) / kHwRows);  // passes
+  int64_t grid = (int64_t)a.cus * 3;  // 3 waves per SIMD at d <= 3072 (165 VGPRs; LDS 39 KB)
+  if (grid > groups) grid = groups;
+  hipLaunchKernelGGL((norm_hw_kernel<MOD, WRITE_Y, KB>), dim3((unsigned)grid), dim3(256), 0,
+                     (hipStream_t)a.stream, (const uint8_t*)a.x, (uint32_t)a.rows, (uint32_t)a.nb,
+                     (uint32_t)(a.ldx * 2), n.shift, n.scale, (uint32_t)n.rows_per_sample, n.eps,
+                     (float)(1.0 / (double)a.d), (const float*)a.t, a.q, (uint32_t)a.ldq, a.s,
+                     (uint32_t)a.lds, a.y, (uint32_t)(a.ldy * 4));
+  return hipGetLastError();
+}
+
+template <bool MOD, bool WRITE_Y>
+hipError_t launch_hw(const NormArgs& n) {
+  const int64_t kb = (n.a.nb + 31) / 32;
+  if (kb <= 1) return launch_hw_t<MOD, WRITE_Y, 1>(n);
+  if (kb == 2) return launch_hw_t<MOD, WRITE_Y, 2>(n);
+  if (kb == 3) return launch_hw_t<MOD, WRITE_Y, 3>(n);
+  return launch_hw_t<MOD, WRITE_Y, 4>(n);
+}
+
 template <int DT, bool MOD, bool WRITE_Y>
 hipError_t launch_t(const NormArgs& n) {
   const LaunchArgs& a = n.a;
@@ -271,6 +467,10 @@ hipError_t launch_t(const NormArgs& n) {
 
 template <bool MOD>
 hipError_t launch_mod(const NormArgs& n) {
+  // bf16 rows of up to 4096 channels: a half wave per row; wider or fp32 rows: the
+  // half waves of a row meet through LDS
+  if (n.a.dtype == DT_BF16 && n.a.nb <= kHwMaxBlocks)
+    return n.a.y ? launch_hw<MOD, true>(n) : launch_hw<MOD, false>(n);
   if (n.a.dtype == DT_BF16)
     return n.a.y ? launch_t<DT_BF16, MOD, true>(n) : launch_t<DT_BF16, MOD, false>(n);
   return n.a.y ? launch_t<DT_FP32, MOD, true>(n) : launch_t<DT_FP32, MOD, false>(n);

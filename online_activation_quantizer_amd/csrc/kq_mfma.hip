@@ -87,13 +87,16 @@ __device__ __forceinline__ void encode_tile(floatx16 acc, int h, uint8_t* qrow, 
   w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, acc[14], acc[15], sc, 3);
   if (S == 255u) w0 = w1 = 0u;
   // h = 0 holds bytes {0,1,4,5 | 8,9,12,13}, h = 1 holds {2,3,6,7 | 10,11,14,15}:
-  // swap one word across halves so lane h stores bytes 8h .. 8h+7 contiguously.
-  const uint32_t recv = (uint32_t)__shfl_xor((int)(h ? w0 : w1), 32);
-  const uint32_t lo = h ? recv : w0, hi = h ? w1 : recv;
-  const uint32_t o0 = (lo & 0xFFFFu) | (hi << 16);
-  const uint32_t o1 = (lo >> 16) | (hi & 0xFFFF0000u);
-  *reinterpret_cast<uint2*>(qrow + 8 * h) = make_uint2(o0, o1);
-  if (h == 0) *srow = (uint8_t)S;
+  // lane h = 0 takes the other half's two words and stores the 16 bytes in one
+  // piece (16-byte stores of 32 rows at the 144-byte pitch meet no LDS bank twice;
+  // 8-byte stores from both halves put rows n and n + 8 on the same banks)
+  const uint32_t r0 = (uint32_t)__shfl_xor((int)w0, 32), r1 = (uint32_t)__shfl_xor((int)w1, 32);
+  if (h == 0) {
+    const uint32_t b0 = (w0 & 0xFFFFu) | (r0 << 16), b1 = (w0 >> 16) | (r0 & 0xFFFF0000u);
+    const uint32_t b2 = (w1 & 0xFFFFu) | (r1 << 16), b3 = (w1 >> 16) | (r1 & 0xFFFF0000u);
+    *reinterpret_cast<u32x4*>(qrow) = u32x4{b0, b1, b2, b3};
+    *srow = (uint8_t)S;
+  }
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -272,7 +272,6 @@ __global__ __launch_bounds__(256) void norm_hw_kernel(
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) float cs[kHwMaxBlocks * kHwStride];
   const uint32_t hw = threadIdx.x >> 5, l = threadIdx.x & 31u;
-
   const uint64_t d = (uint64_t)nb * kBlk;
   // the sample whose constants are in LDS (none yet)
   uint64_t cur_g = ~0ull;

@@ -37,7 +37,7 @@ KERNELS = [
      FLUX_E // 2 + FLUX_E // 32, "hq_quantize (block Hadamard), 4608x3072 bf16"),
     ("sq", "void kq::(anonymous namespace)::sq_kernel<0, false>", FLUX_E * 2 + 3072 * 4,
      FLUX_E // 2 + FLUX_E // 32, "sq_quantize (SmoothQuant), 4608x3072 bf16"),
-    ("norm", "void kq::(anonymous namespace)::norm_kernel<0, true, false>", FLUX_E * 2 + 2 * 3072 * 4 + 96 * 60,
+    ("norm", "void kq::(anonymous namespace)::norm_hw_kernel<true, false, 3>", FLUX_E * 2 + 2 * 3072 * 4 + 96 * 60,
      FLUX_E // 2 + FLUX_E // 32, "kq_norm_quantize (LayerNorm + modulation fused), 4608x3072 bf16"),
     ("weights", "void kq::(anonymous namespace)::butterfly_kernel<0, false, 1>", WEIGHT_E * 2 + 96 * 60,
      WEIGHT_E // 2 + WEIGHT_E // 32, "kq_quantize_weights, 12288x3072 bf16"),
@@ -128,7 +128,8 @@ TRACE_KERNELS = [
     ("void kq::(anonymous namespace)::butterfly_kernel<0, false, 2>", "`butterfly_kernel<bf16, -, hadamard>` (hq_quantize)"),
     ("void kq::(anonymous namespace)::sq_kernel<0, false>", "`sq_kernel<bf16>` (sq_quantize)"),
     ("(anonymous namespace)::stream_kernel", "`stream_kernel` (same-bytes ceiling, 5 grid sizes; when traced)"),
-    ("void kq::(anonymous namespace)::norm_kernel<0, true, false>", "`norm_kernel<bf16, modulated>` (kq_norm_quantize)"),
+    ("void kq::(anonymous namespace)::norm_hw_kernel<true, false, 3>",
+     "`norm_hw_kernel<modulated, -, 3 blocks per lane>` (kq_norm_quantize)"),
     ("void kq::(anonymous namespace)::butterfly_kernel<0, false, 1>",
      "`butterfly_kernel<bf16, -, weights>` (kq_quantize_weights, 12288x3072)"),
     ("gemm unsplit 216", "`mx_gemm_kernel<256x256 tiles, bf16 out, staged>` (kq_mx_gemm, 4608x12288x3072, 216 workgroups)"),
@@ -206,8 +207,9 @@ CLOCK_KERNELS = [
     ("(anonymous namespace)::stream_ring_kernel", "same bytes, two units in flight"),
     ("(anonymous namespace)::stream_read_kernel", "read half alone"),
     ("(anonymous namespace)::stream_write_kernel", "write half alone"),
+    ("void kq::(anonymous namespace)::norm_hw_kernel<true, false, 3>", "kq_norm_quantize (fused norm)"),
 ]
-CLOCK_CMD = ("python3 bench.py --steps 20 --warmup 5 --no-cpu --eager --no-weights --no-norm --no-gemm --no-mlp "
+CLOCK_CMD = ("python3 bench.py --steps 20 --warmup 5 --no-cpu --eager --no-weights --no-gemm --no-mlp "
              "--no-shard --no-quality --no-sweep --no-overlap")
 CLOCK_COUNTERS = "GRBM_GUI_ACTIVE SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY"
 
@@ -277,7 +279,7 @@ def counters(out_md, title, commands, dirs):
     under profiles/ with the commands that produced the runs."""
     known = [(k, v) for k, v in CLOCK_KERNELS] + [
         ("void kq::(anonymous namespace)::mfma_kernel<false>", "matrix-core kq_quantize (design A)"),
-        ("void kq::(anonymous namespace)::norm_kernel<0, true, false>", "kq_norm_quantize (fused norm)"),
+        ("void kq::(anonymous namespace)::norm_hw_kernel<true, false, 3>", "kq_norm_quantize (fused norm)"),
         ("void kq::(anonymous namespace)::mx_gemm_kernel<", "kq_mx_gemm (W4A4 product)")]
     per = {}
     for dd in dirs:

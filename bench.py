@@ -530,10 +530,12 @@ def gemm_timing(args, qs, ss):
 
 
 def gemm_split_timing(args):
-    """A product with few tiles and a long K, where splitting each tile in two K
-    halves (kq_mx_gemm_ws, through a workspace) pays: the FLUX MLP down-projection
-    for 1024 tokens, Y[1024, 3072] = deq(Qx)[1024, 12288] deq(Qw)[3072, 12288]^T
-    (48 tiles of 256 x 256 on 256 compute units), bf16 out; unsplit beside it."""
+    """A product with few tiles and a long K, where splitting each tile in K parts
+    (kq_mx_gemm_ws, through a workspace) pays: the FLUX MLP down-projection for
+    1024 tokens, Y[1024, 3072] = deq(Qx)[1024, 12288] deq(Qw)[3072, 12288]^T (48
+    tiles of 256 x 256 on 256 compute units), bf16 out; unsplit beside it, and
+    kq_mx_gemm_static (the library's static array: fewer part slots, so fewer
+    parts)."""
     import torch
 
     import synth
@@ -549,9 +551,11 @@ def gemm_split_timing(args):
     ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device="cuda")
     out, out_ws = (torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(2))
     steps = max(8, args.steps // 10)
+    out_st = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     legs = {}
     for name, fn in (("unsplit", lambda i: kq.kq_mx_gemm(qx, sx, qw, sw, out=out)),
-                     ("split", lambda i: kq.kq_mx_gemm_ws(qx, sx, qw, sw, ws, out=out_ws))):
+                     ("split", lambda i: kq.kq_mx_gemm_ws(qx, sx, qw, sw, ws, out=out_ws)),
+                     ("static", lambda i: kq.kq_mx_gemm_static(qx, sx, qw, sw, out=out_st))):
         ms = (timed(fn, steps, args.warmup, torch.cuda.current_stream()) if args.eager
               else timed_graph(fn, steps, min(args.warmup, 10)))
         leg = {"ms_per_call": round(ms, 6), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
@@ -560,10 +564,17 @@ def gemm_split_timing(args):
         legs[name] = leg
     torch.cuda.synchronize()
     rel = float((out_ws.float() - out.float()).norm() / out.float().norm())
+    rel_st = float((out_st.float() - out.float()).norm() / out.float().norm())
+    # K parts per tile: the workspace holds one 256 KiB slot per part of every tile;
+    # the static array 128 slots
+    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+    parts = (nbytes - 4096) // (tiles * 256 * 256 * 4) if nbytes else 1
     return {"workload": f"FLUX.1-schnell MLP down-projection, 1024 tokens: {M}x{N}x{K}, bf16 out",
-            "entry": "kq_mx_gemm_ws", "workspace_bytes": nbytes, **legs,
+            "entry": "kq_mx_gemm_ws", "workspace_bytes": nbytes,
+            "parts": {"split": parts, "static": min(parts, 128 // tiles)}, **legs,
             "t_split_over_t_unsplit": round(legs["split"]["ms_per_call"] / legs["unsplit"]["ms_per_call"], 4),
-            "rel_diff_vs_unsplit": round(rel, 6)}
+            "t_static_over_t_unsplit": round(legs["static"]["ms_per_call"] / legs["unsplit"]["ms_per_call"], 4),
+            "rel_diff_vs_unsplit": round(rel, 6), "static_rel_diff_vs_unsplit": round(rel_st, 6)}
 
 
 def gemm_fused_timing(args):

@@ -251,11 +251,14 @@ int kq_mx_gemm_fused(const void* x, int dtype, int64_t ldx, const float* params,
  * the same product as kq_mx_gemm).  The product computes 256 x 256 output tiles, at
  * most one workgroup per compute unit.  When twice the tiles (rounded up to a
  * multiple of 8) fit on the compute units and K has at least 10 steps of 256,
- * each tile is computed as two halves of K on two compute units, which meet
- * through the workspace: 4096 bytes of flag words, then 256 KiB of fp32 partial
- * sums per tile (1024 x 3072 x 12288: 48 tiles, 12 MiB, 0.70x the unsplit time).
- * With more tiles the matrix cores are already busy on most compute units and
- * nothing is split.
+ * each tile is computed as S parts of K on S compute units of one XCD, which meet
+ * through the workspace: S is the largest of 2, 4 and 8 such that S times the
+ * tiles (rounded up to 8) fit on the compute units and every part has at least 5
+ * K steps.  The workspace is 4096 bytes of flag words, then S x 256 KiB of fp32
+ * partial sums per tile (1024 x 3072 x 12288: 48 tiles, S = 4, 48 MiB, 0.57x the
+ * unsplit time).  The parts' sums are added in part order, so the result does not
+ * depend on the order in which they finish.  With more tiles the matrix cores are
+ * already busy on most compute units and nothing is split.
  * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_HIP. */
 int kq_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes);
 
@@ -275,16 +278,17 @@ int kq_mx_gemm_ws(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t lds
 
 /* kq_mx_gemm_ws without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, serving loops, harnesses that
- * forbid allocation): same arguments, result and errors as kq_mx_gemm, and it
- * allocates nothing.  The split tiles meet through the library's own static
- * device array of 4096 + 128 x 256 KiB bytes (32 MiB + 4 KiB), which every device
- * the library runs on holds until the process ends; a shape that would need more
- * (more than 128 split tiles, only on devices of more than 256 compute units)
- * returns KQ_ERR_VALUE.  The array's address is looked up on a device's first
- * call, which also clears its flag words with a kernel on `stream`.  Every call on
- * one device shares that device's array: calls that overlap on one device (other
- * streams, other threads) race and must not be made.
- * Errors: as kq_mx_gemm, and KQ_ERR_VALUE. */
+ * forbid allocation): same arguments and errors as kq_mx_gemm, and it allocates
+ * nothing.  The split tiles meet through the library's own static device array of
+ * 4096 + 128 x 256 KiB bytes (32 MiB + 4 KiB), which every device the library
+ * runs on holds until the process ends.  Its 128 slots of partial sums bound the
+ * parts: the tiles are split as kq_mx_gemm_ws splits them when S x tiles <= 128,
+ * else in the largest of 4 and 2 parts that fits (the same result up to the fp32
+ * rounding of the parts' sums), else not at all.  The array's address is looked
+ * up on a device's first call, which also clears its flag words with a kernel on
+ * `stream`.  Every call on one device shares that device's array: calls that
+ * overlap on one device (other streams, other threads) race and must not be made.
+ * Errors: as kq_mx_gemm. */
 int kq_mx_gemm_static(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
                       const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
                       int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream);

@@ -384,8 +384,8 @@ int kq_mx_gemm_static(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t
   int cus = 0;
   rc = current_cus(&cus);
   if (rc != KQ_OK) return rc;
-  const int64_t need = kq::mx_gemm_workspace_bytes(M, N, K, cus);
-  if (need > kq::kStaticScratchBytes) return KQ_ERR_VALUE;
+  // the split schedule whose part slots the static array holds
+  const int64_t need = kq::mx_gemm_workspace_bytes(M, N, K, cus, kq::kStaticSplitTiles);
   void* ws = nullptr;
   if (need > 0) {
     const hipError_t e = kq::static_scratch(&ws, stream);

@@ -32,10 +32,10 @@
 // per-tile range) and are not stored; K-blocks past K get scale 2^-127 on both
 // operands (their products vanish).
 //
-// Split tiles.  With a caller's workspace and few tiles (at most half the compute
-// units busy) and a long K, each tile is computed as two K halves on two
-// workgroups of its XCD; the first to finish stores its fp32 sums, the second adds
-// them to its own and writes the tile (kernel variant SPLIT).
+// Split tiles.  With a workspace and few tiles (at most half the compute units
+// busy) and a long K, each tile is computed as S parts of K on S workgroups of its
+// XCD; every part but the last to finish stores its fp32 sums, and the last adds
+// all parts in part order and writes the tile (kernel variant SPLIT).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -100,13 +100,16 @@ constexpr int kEpiScalar = 0, kEpiVec4 = 1, kEpiStaged = 2;
 // marks a tile written from its accumulators alone
 struct NoPartial {};
 
+// the most K parts a split tile runs in (the exchange loads one slot per part)
+constexpr int kSplitMaxPartsDev = 8;
+
 
 template <class T, bool OUT_BF16, int EPI, bool SCALE_WORDS, bool SPLIT>
 __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void mx_gemm_kernel(
     const uint8_t* __restrict__ qa, uint32_t lda, const uint8_t* __restrict__ sa, uint32_t ldsa,
     const uint8_t* __restrict__ qb, uint32_t ldb, const uint8_t* __restrict__ sb, uint32_t ldsb,
     uint32_t M, uint32_t N, uint32_t K, void* __restrict__ out, uint32_t ldo, uint32_t tiles_n,
-    uint32_t ntiles, uint32_t xcd_cols, uint32_t pair_off, uint32_t* __restrict__ flags,
+    uint32_t ntiles, uint32_t xcd_cols, uint32_t parts, uint32_t* __restrict__ flags,
     float* __restrict__ partials) {
   constexpr int kRows = T::kRows, kBM = T::kBM, kThreads = T::kThreads;
   static_assert(EPI != kEpiStaged || (OUT_BF16 && T::kCanStage), "staged output: bf16, tiles that fit");
@@ -299,12 +302,12 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
 
   // acc[i][j][4 q + e]: Y row lr of the wave's A tile i, column 8 q + 4 h + e of its
   // B tile j
-  // `add` is NoPartial, or gives the 4 sums of the other K half of a split tile to
-  // add to the outputs acc[i][j][4 q .. 4 q + 3] as they are written
+  // `add` is NoPartial, or turns this workgroup's sums acc[i][j][4 q .. 4 q + 3]
+  // into the whole split tile's (all K parts) as they are written
   auto outputs = [&](auto add, int i, int j, int q) -> f32x4 {
     const f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     if constexpr (std::is_same_v<decltype(add), NoPartial>) return v;
-    else return v + add(i, j, q);
+    else return add(i, j, q, v);
   };
   auto write_tile = [&](uint32_t t, auto add) {
     uint32_t m0, n0;
@@ -405,23 +408,21 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
 
   // The work of this workgroup.  Whole tiles: tiles blockIdx.x, + grid, ...
   // (my_tiles of them), nsteps K steps each.  SPLIT (fewer tiles than half the
-  // grid): one K half of one tile, workgroup b < ntiles taking steps [0, nsteps / 2)
-  // of tile b and workgroup pair_off + b steps [nsteps / 2, nsteps) (pair_off a
-  // multiple of 8, so both run on the tile's XCD); the other workgroups have
-  // nothing to do.
+  // grid): one K part of one tile, workgroup p n8 + t (n8 = ntiles rounded up to
+  // 8, so all parts of a tile run on its XCD) taking steps
+  // [p nsteps / parts, (p + 1) nsteps / parts) of tile t; workgroups past the
+  // tiles have nothing to do.
   const uint32_t wg = blockIdx.x;
   uint32_t l_tile = wg, l_step = 0, l_end = nsteps;  // the step the next load fetches (split: [l_step, l_end))
+  [[maybe_unused]] uint32_t part = 0;
   uint64_t total;
   if constexpr (SPLIT) {
-    const uint32_t mid = nsteps / 2u;
-    if (wg < ntiles) {
-      l_end = mid;
-    } else if (wg >= pair_off && wg - pair_off < ntiles) {
-      l_tile = wg - pair_off;
-      l_step = mid;
-    } else {
-      return;
-    }
+    const uint32_t n8 = (ntiles + 7u) & ~7u;
+    part = wg / n8;
+    l_tile = wg - part * n8;
+    if (l_tile >= ntiles || part >= parts) return;
+    l_step = (uint32_t)((uint64_t)part * nsteps / parts);
+    l_end = (uint32_t)((uint64_t)(part + 1u) * nsteps / parts);
     total = l_end - l_step;
   } else {
     total = (uint64_t)((ntiles - 1u - wg) / grid + 1u) * nsteps;  // grid <= ntiles
@@ -496,30 +497,33 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   }
   if constexpr (!SPLIT) return;
 
-  // The two halves of a split tile meet through its flag word and one fp32 tile of
-  // partial sums (thread tid's accumulators as 16-byte pieces, piece p at
-  // p kThreads + tid).  Each half adds 1 to the flag on arrival (bits 0-1 count the
-  // arrivals).  The first to arrive (old value 0) stores its sums, waits until they
-  // are visible to the device and adds kReady; the second (old value 1 or 1 + kReady)
-  // waits for kReady, which comes from a workgroup that is already running and
-  // waits for nothing, adds the stored sums to its own, puts the flag back to 0 for
-  // the next call and writes the tile.  No workgroup waits for one that may not
-  // have started, whatever the order workgroups run in.
-  constexpr uint32_t kReady = 4u;
+  // The parts of a split tile meet through its flag word and one fp32 tile of
+  // partial sums per part (thread tid's accumulators as 16-byte pieces, piece c at
+  // c kThreads + tid).  Each part adds 1 to the flag on arrival (bits 0-7 count
+  // the arrivals).  Every part but the last to arrive stores its sums in its own
+  // slot, waits until they are visible to the device and adds kReady (bits 8-15
+  // count the stored parts); the last waits for parts - 1 stored parts, which come
+  // from workgroups already running that wait for nothing, adds every part's sums
+  // in part order (its own from registers), so the result does not depend on the
+  // order of arrival, puts the flag back to 0 for the next call and writes the
+  // tile.  No workgroup waits for one that may not have started, whatever the
+  // order workgroups run in.
+  constexpr uint32_t kReady = 256u;
   __shared__ uint32_t arrival;
-  const uint32_t sidx = h_tile;
-  uint32_t* flag = flags + sidx;
-  // the tile's sums through one buffer descriptor: piece p of this thread at byte
-  // offset 16 tid (per lane) + 16 kThreads p (per instruction).  They are stored and
-  // loaded device-coherent (cache policy sc1, the form of agent-scope relaxed
-  // atomics), so they need no cache write-back or invalidation, which would also
-  // drop the other workgroups' operands from the XCD's L2.
+  uint32_t* flag = flags + h_tile;
+  // the tile's part slots through one buffer descriptor: piece c of part p's slot
+  // for this thread at byte offset 16 tid (per lane) + 16 kThreads c + p x tile
+  // bytes (per instruction).  They are stored and loaded device-coherent (cache
+  // policy sc1, the form of agent-scope relaxed atomics), so they need no cache
+  // write-back or invalidation, which would also drop the other workgroups'
+  // operands from the XCD's L2.
+  constexpr int kTileBytes = kBM * T::kBN * 4;
   const __amdgpu_buffer_rsrc_t rsrc_p = __builtin_amdgcn_make_buffer_rsrc(
-      partials + (uint64_t)sidx * (kBM * T::kBN), 0, kBM * T::kBN * 4, 0x00020000);
+      partials + (uint64_t)h_tile * parts * (kBM * T::kBN), 0, (int)(parts * (uint32_t)kTileBytes), 0x00020000);
   constexpr int kDeviceCoherent = 16;  // sc1
   if (tid == 0) arrival = __hip_atomic_fetch_add(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (__builtin_amdgcn_readfirstlane(arrival) == 0u) {
+  if ((__builtin_amdgcn_readfirstlane(arrival) & 0xFFu) + 1u < parts) {
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i)
 #pragma unroll
@@ -528,7 +532,8 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
         for (int q = 0; q < 4; ++q) {
           const f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsrc_p, (int)(16u * tid),
-                                                 16 * kThreads * ((i * T::kTN + j) * 4 + q),
+                                                 (int)(part * (uint32_t)kTileBytes) +
+                                                     16 * kThreads * ((i * T::kTN + j) * 4 + q),
                                                  kDeviceCoherent);
         }
     // every wave's stores complete (visible device-wide) before the flag changes
@@ -540,22 +545,54 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
     return;
   }
   if (tid == 0) {
-    // bounded: the first half has arrived and only stores its sums before kReady
+    // bounded: the other parts have arrived and only store their sums before kReady
     for (uint32_t n = 0; n < (1u << 26); ++n) {
-      if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kReady) break;
+      if (((__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 8) & 0xFFu) + 1u >= parts)
+        break;
       __builtin_amdgcn_s_sleep(2);
     }
   }
   __syncthreads();
   if (tid == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  auto stored_sums = [&](int i, int j, int q) {
-    return __builtin_bit_cast(
-        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_p, (int)(16u * tid),
-                                                     16 * kThreads * ((i * T::kTN + j) * 4 + q),
-                                                     kDeviceCoherent));
+  // The tile's sums, parts 0, 1, ... added in that order (the order of arrival
+  // does not matter).  The other parts' slots are loaded branch-free, NO of them
+  // per piece, NO = 1, 3 or 7 (the schedule makes it parts - 1; were it more, the
+  // loads past the last part would be addressed outside the descriptor's range
+  // and return zeros, which add exactly, the sums never being -0 since every
+  // accumulation starts at +0).  Other slot k is part k, or k + 1 from this part
+  // on.
+  auto all_parts_n = [&](auto no_c) {
+    return [&](int i, int j, int q, const f32x4& own) {
+      constexpr int NO = decltype(no_c)::value;
+      const int piece = 16 * kThreads * ((i * T::kTN + j) * 4 + q);
+      f32x4 x[NO];
+#pragma unroll
+      for (int k = 0; k < NO; ++k) {
+        const uint32_t pp = (uint32_t)k < part ? (uint32_t)k : (uint32_t)k + 1u;
+        // (the whole offset per lane, where the range check applies)
+        x[k] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rsrc_p, (int)(16u * tid) + (pp < parts ? (int)pp * kTileBytes + piece : 1 << 30), 0,
+                       kDeviceCoherent));
+      }
+      f32x4 sum = part == 0u ? own : x[0];
+#pragma unroll
+      for (int pp = 1; pp <= NO; ++pp) {
+        // slot pp holds part pp below this part, slot pp - 1 part pp above it (pp = NO
+        // is never below: part <= parts - 1 <= NO)
+        const f32x4& below = x[pp < NO ? pp : NO - 1];
+        sum += (uint32_t)pp == part ? own : (uint32_t)pp < part ? below : x[pp - 1];
+      }
+      return sum;
+    };
   };
-  if (EPI == kEpiStaged) write_tile_staged(h_tile, 0, stored_sums);
-  else write_tile(h_tile, stored_sums);
+  auto write = [&](auto add) {
+    if (EPI == kEpiStaged) write_tile_staged(h_tile, 0, add);
+    else write_tile(h_tile, add);
+  };
+  if (parts <= 2u) write(all_parts_n(std::integral_constant<int, 1>{}));
+  else if (parts <= 4u) write(all_parts_n(std::integral_constant<int, 3>{}));
+  else write(all_parts_n(std::integral_constant<int, kSplitMaxPartsDev - 1>{}));
 }
 
 // The static split workspace (kq_mx_gemm_static): zero-initialized with the
@@ -598,18 +635,20 @@ hipError_t static_scratch(void** ptr, void* stream) {
 // The grid and the tiles' order for one product (the kernel's unit list).
 struct Schedule {
   int64_t tiles_n, ntiles, grid, xcd_cols;
-  bool split;        // every tile in two K halves through the workspace
-  int64_t pair_off;  // workgroup of a tile's second half, past the first's
+  bool split;     // every tile in `parts` K parts through the workspace
+  int64_t parts;  // K parts per tile (split), workgroup p n8 + t taking part p of tile t
 };
 
-// Tiles are split in K halves only when at least this many K steps (of 256
-// values) make a half worth the exchange of partial sums (split against unsplit:
-// 4096 x 1152 x 1152, 5 steps: 1.34x the time; 2048 x 2240 x 2240, 9 steps:
-// 0.95-1.01x; 256 x 256 x 3072, 12 steps: 0.82-0.85x; 1024 x 3072 x 12288, 48
-// steps: 0.70x).
-constexpr int64_t kSplitMinSteps = 10;
+// Tiles are split in K only into parts of at least this many K steps (of 256
+// values), which make a part worth the exchange of partial sums (two halves
+// against the unsplit tile: 4096 x 1152 x 1152, 5 steps: 1.34x the time; 2048 x
+// 2240 x 2240, 9 steps: 0.95-1.01x; 256 x 256 x 3072, 12 steps: 0.82-0.85x; 1024
+// x 3072 x 12288, 48 steps: 0.70x), and into at most kSplitMaxParts parts.
+constexpr int64_t kSplitMinStepsPerPart = 5;
+constexpr int64_t kSplitMaxParts = kSplitMaxPartsDev;
 
-Schedule make_schedule(int64_t M, int64_t N, int64_t K, int cus, bool allow_split) {
+// max_slots: the partial-sum tiles the workspace holds (0: whole tiles only).
+Schedule make_schedule(int64_t M, int64_t N, int64_t K, int cus, int64_t max_slots) {
   using T = ProductTiling;
   Schedule s{};
   const int64_t tiles_m = (M + T::kBM - 1) / T::kBM;
@@ -624,16 +663,30 @@ Schedule make_schedule(int64_t M, int64_t N, int64_t K, int cus, bool allow_spli
   // idle: with whole rounds of tiles on (nearly) all of them, the matrix cores are
   // power-limited (4608 x 12288 x 3072: the shader clock falls from 1.92 GHz with
   // 216 busy compute units to 1.45-1.69 with 256), so more busy units bring no more
-  // throughput, and splitting only adds the exchange.
-  s.split = allow_split && 2 * n8 <= full_grid && s.ntiles <= kSplitMaxTiles && nsteps >= kSplitMinSteps;
+  // throughput, and splitting only adds the exchange.  So: the largest power of
+  // two of parts that fits the compute units, with parts of at least
+  // kSplitMinStepsPerPart steps, at most kSplitMaxParts, and no more than the
+  // workspace holds (one slot per part of every tile).  Powers of two because the
+  // last part loads the other parts' slots as 1, 3 or 7 loads per piece, and a
+  // count between (a load returning zeros still costs address processing)
+  // measured slower: 1024 x 3072 x 12288 in 2, 3, 4 and 5 parts 59.8, 51.5, 48.7
+  // and 56.5 us (unsplit 85.1); 512 x 512 x 12288 in 2, 4 and 8 parts 47.2, 38.0
+  // and 37.5 us (unsplit 79.3).
+  int64_t parts = full_grid / n8;
+  parts = parts < nsteps / kSplitMinStepsPerPart ? parts : nsteps / kSplitMinStepsPerPart;
+  parts = parts < kSplitMaxParts ? parts : kSplitMaxParts;
+  const int64_t fit = s.ntiles > 0 ? max_slots / s.ntiles : 0;
+  parts = parts < fit ? parts : fit;
+  parts = parts >= 8 ? 8 : parts >= 4 ? 4 : parts >= 2 ? 2 : parts;
+  s.split = parts >= 2 && s.ntiles <= kSplitMaxTiles;
   if (s.split) {
-    s.pair_off = n8;
-    s.grid = 2 * n8;
+    s.parts = parts;
+    s.grid = parts * n8;
   } else {
     // no more workgroups than keep the number of tile rounds, so every workgroup
     // runs the same number of tiles up to one (4608 x 12288: 864 tiles, 216
     // workgroups of 4 instead of 256 of 3 or 4: 121.9 -> 120.1 us)
-    s.pair_off = 0;
+    s.parts = 1;
     s.grid = full_grid < s.ntiles ? full_grid : s.ntiles;
     const int64_t rounds = (s.ntiles + s.grid - 1) / s.grid;
     int64_t even = (s.ntiles + rounds - 1) / rounds;
@@ -644,9 +697,9 @@ Schedule make_schedule(int64_t M, int64_t N, int64_t K, int cus, bool allow_spli
   return s;
 }
 
-int64_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus) {
-  const Schedule s = make_schedule(M, N, K, cus, true);
-  return s.split ? kSplitFlagBytes + s.ntiles * kSplitTileBytes : 0;
+int64_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus, int64_t max_slots) {
+  const Schedule s = make_schedule(M, N, K, cus, max_slots);
+  return s.split ? kSplitFlagBytes + s.parts * s.ntiles * kSplitTileBytes : 0;
 }
 
 template <class T, bool OUT_BF16, int EPI, bool SCALE_WORDS, bool SPLIT>
@@ -656,7 +709,7 @@ void launch_t(const GemmArgs& g, const Schedule& s) {
                      dim3(T::kThreads), 0, (hipStream_t)g.stream, g.qa, (uint32_t)g.lda, g.sa,
                      (uint32_t)g.ldsa, g.qb, (uint32_t)g.ldb, g.sb, (uint32_t)g.ldsb, (uint32_t)g.M,
                      (uint32_t)g.N, (uint32_t)g.K, g.out, (uint32_t)g.ldo, (uint32_t)s.tiles_n,
-                     (uint32_t)s.ntiles, (uint32_t)s.xcd_cols, (uint32_t)s.pair_off,
+                     (uint32_t)s.ntiles, (uint32_t)s.xcd_cols, (uint32_t)s.parts,
                      reinterpret_cast<uint32_t*>(ws),
                      ws ? reinterpret_cast<float*>(ws + kSplitFlagBytes) : nullptr);
 }
@@ -674,10 +727,11 @@ void launch_w(const GemmArgs& g, bool words, const Schedule& s) {
 
 hipError_t launch_mx_gemm(const GemmArgs& g) {
   using T = ProductTiling;
-  // the split schedule only with a workspace that holds it
-  const bool split = g.workspace != nullptr &&
-                     g.workspace_bytes >= mx_gemm_workspace_bytes(g.M, g.N, g.K, g.cus);
-  const Schedule s = make_schedule(g.M, g.N, g.K, g.cus, split);
+  // split tiles only as far as the workspace holds their parts
+  const int64_t slots = g.workspace != nullptr && g.workspace_bytes >= kSplitFlagBytes
+                            ? (g.workspace_bytes - kSplitFlagBytes) / kSplitTileBytes
+                            : 0;
+  const Schedule s = make_schedule(g.M, g.N, g.K, g.cus, slots);
   // whole 32-bit scale words when every scale row starts 4-byte aligned and holds one
   const bool words = ((uintptr_t)g.sa % 4 == 0) && ((uintptr_t)g.sb % 4 == 0) && g.ldsa % 4 == 0 &&
                      g.ldsb % 4 == 0 && g.K >= 128;

@@ -55,24 +55,24 @@ struct GemmArgs {
   bool out_bf16;
   void* stream;
   int cus;       // compute units of the device (persistent grid size)
-  // device workspace for tiles split in K halves (flags first, zero between
-  // calls), or NULL for whole tiles only; used when it holds
-  // mx_gemm_workspace_bytes()
+  // device workspace for tiles split in K parts (flags first, zero between calls),
+  // or NULL for whole tiles only; tiles are split only as far as it holds their
+  // parts (all of mx_gemm_workspace_bytes() when it holds that much)
   void* workspace = nullptr;
   int64_t workspace_bytes = 0;
 };
 
 // Workspace of the W4A4 product's split tiles: kSplitFlagBytes of flags (one
 // 32-bit word per split tile, zero between calls), then one 256 x 256 fp32 tile of
-// partial sums per split tile.
+// partial sums (a slot) per K part of every split tile.
 constexpr int64_t kSplitFlagBytes = 4096;
 constexpr int64_t kSplitMaxTiles = kSplitFlagBytes / 4;
 constexpr int64_t kSplitTileBytes = 256 * 256 * 4;
 
 // The library's own split workspace for callers that cannot allocate: a static
 // device array of kStaticScratchBytes on every device the library runs on (flags,
-// then the partial sums of up to kStaticSplitTiles tiles, the most a device of 256
-// compute units splits).
+// then kStaticSplitTiles slots of partial sums: on a device of 256 compute units,
+// every split schedule of two parts fits, and more parts as far as they fit).
 constexpr int64_t kStaticSplitTiles = 128;
 constexpr int64_t kStaticScratchBytes = kSplitFlagBytes + kStaticSplitTiles * kSplitTileBytes;
 // Device address of the current device's static workspace (set up on its first
@@ -130,8 +130,11 @@ hipError_t launch_hadamard(const LaunchArgs& a);  // fixed block-Hadamard, then 
 hipError_t launch_norm(const NormArgs& n);        // LayerNorm + modulation, T_b, MXFP4
 hipError_t launch_mx_gemm(const GemmArgs& g);    // Y = deq(A) deq(B)^T on scaled MFMA
 hipError_t launch_mx_gemm_fused(const FusedGemmArgs& g);  // Y = deq(Q(T X)) deq(B)^T
-// bytes of workspace the product's split tiles need (0: nothing is split)
-int64_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus);
+// Workspace bytes of the split schedule of an M x N x K product on `cus` compute
+// units whose workspace holds at most max_slots partial-sum slots (0 if its tiles
+// are not split).
+int64_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus,
+                                int64_t max_slots = INT64_MAX);
 hipError_t launch_sq(const LaunchArgs& a);
 hipError_t launch_mfma(const LaunchArgs& a);
 hipError_t launch_expand(const float* params, int64_t nb, int tfmt, void* out, void* stream);

@@ -488,7 +488,7 @@ def kq_mx_gemm_workspace_size(M: int, N: int, K: int) -> int:
 
 
 def kq_mx_gemm_ws(qa, sa, qb, sb, workspace, out=None, out_dtype=None, stream=None):
-    """kq_mx_gemm with each output tile split in two K halves through
+    """kq_mx_gemm with each output tile split into 2, 4 or 8 parts of K through
     ``workspace`` when the library's rule splits the shape (uint8 device tensor of
     kq_mx_gemm_workspace_size bytes whose first 4096 bytes are zero before the
     first call; every call leaves them zero).  ``workspace=None`` runs the unsplit

@@ -2,12 +2,15 @@
 reference, through the C ABI.
 
 When the 256 x 256 output tiles leave at least half of the compute units idle and
-a tile has at least 10 K steps (256 values each), each tile is computed as two
-halves of K on two workgroups that meet through the caller's workspace.  The fp32
-sum of the two half sums has one more rounding than the unsplit product, inside
-the same bound as kq_mx_gemm's tests, (K/64 + 2) 2^-23 sum_k |a_k b_k|.  The
-workspace's flag words start at zero and every call leaves them zero, so calls in
-a row, on shapes of different sizes, share one workspace.
+a tile has at least 10 K steps (256 values each), each tile is computed as S parts
+of K on S workgroups that meet through the caller's workspace: S is the largest
+power of two (2, 4 or 8) of parts that fit the compute units, each of at least 5
+K steps.  Every part's
+fp32 sums are added in part order, one rounding per addition more than the
+unsplit product: the bound is (K/64 + S) 2^-23 sum_k |a_k b_k| (the unsplit
+product's tests use S = 2).  The workspace's flag words start at zero and every
+call leaves them zero, so calls in a row, on shapes of different sizes, share one
+workspace.
 """
 import numpy as np
 import pytest
@@ -22,7 +25,8 @@ pytestmark = pytest.mark.gpu
 
 FLAG_BYTES = 4096
 TILE_BYTES = 256 * 256 * 4
-MIN_STEPS = 10  # K steps per tile from which the library splits
+MIN_STEPS_PER_PART = 5  # K steps per part from which the library splits
+MAX_PARTS = 8
 
 
 def cus():
@@ -34,24 +38,30 @@ def tiles(M, N):
     return ((M + 255) // 256) * ((N + 255) // 256)
 
 
-def split_expected(M, N, K):
+def parts_expected(M, N, K, max_slots=None):
     """The rule the library states: one workgroup per compute unit (a multiple of
-    8); split when twice the tiles (rounded up to 8) fit in that grid and a tile
-    has at least 10 K steps."""
+    8); the largest power of two of parts per tile that fits that grid (tiles
+    rounded up to 8), with parts of at least 5 K steps, at most 8, and no more
+    than the workspace's part slots; split when that is at least two.  Returns 1
+    for whole tiles."""
     full = max(8, cus() // 8 * 8)
     n8 = (tiles(M, N) + 7) // 8 * 8
-    return 2 * n8 <= full and tiles(M, N) <= FLAG_BYTES // 4 and (K + 255) // 256 >= MIN_STEPS
+    p = min(full // n8, ((K + 255) // 256) // MIN_STEPS_PER_PART, MAX_PARTS)
+    if max_slots is not None:
+        p = min(p, max_slots // tiles(M, N))
+    p = 8 if p >= 8 else 4 if p >= 4 else 2 if p >= 2 else p
+    return p if p >= 2 and tiles(M, N) <= FLAG_BYTES // 4 else 1
 
 
 def workspace_for(M, N, K):
     import torch
     n = kq.kq_mx_gemm_workspace_size(M, N, K)
-    split = split_expected(M, N, K)
-    assert n == (FLAG_BYTES + tiles(M, N) * TILE_BYTES if split else 0), (M, N, K, n, split)
-    return torch.zeros(max(n, FLAG_BYTES), dtype=torch.uint8, device="cuda"), split
+    parts = parts_expected(M, N, K)
+    assert n == (FLAG_BYTES + parts * tiles(M, N) * TILE_BYTES if parts > 1 else 0), (M, N, K, n, parts)
+    return torch.zeros(max(n, FLAG_BYTES), dtype=torch.uint8, device="cuda"), parts
 
 
-def run_case(M, N, K, ws, seed, label):
+def run_case(M, N, K, ws, parts, seed, label):
     import torch
     rng = np.random.default_rng(seed)
     qa, sa = random_mx(M, K, rng)
@@ -62,20 +72,34 @@ def run_case(M, N, K, ws, seed, label):
     torch.cuda.synchronize()
     assert torch.equal(y32.to(torch.bfloat16), y16), label
     Yref, Yabs = oracle.mx_gemm(qa, sa, qb, sb)
-    check(host(y32), Yref, Yabs, K, label)
+    check(host(y32), Yref, Yabs, K, label, parts=max(2, parts))
     assert int(ws[:FLAG_BYTES].count_nonzero()) == 0, f"{label}: flags not left at zero"
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 2560), (512, 512, 2560), (300, 520, 2336), (257, 257, 2592),
                                    (1000, 776, 3072), (64, 1030, 2400), (256, 2048, 2560)])
 def test_split_halves(M, N, K):
-    """Fewer tiles than half the compute units: every tile in two halves of K
-    (ragged M, N and K included; N = 1030 takes the one-output-per-store path;
-    2048 columns deal the tiles to the XCDs)."""
+    """Fewer tiles than half the compute units and 10-14 K steps: every tile in two
+    parts of K (ragged M, N and K included; N = 1030 takes the one-output-per-store
+    path; 2048 columns deal the tiles to the XCDs)."""
     say(f"[mx gemm split halves] {M}x{N}x{K}")
-    ws, split = workspace_for(M, N, K)
-    assert split
-    run_case(M, N, K, ws, M * 5 + N * 3 + K, f"halves {M}x{N}x{K}")
+    ws, parts = workspace_for(M, N, K)
+    assert parts == 2
+    run_case(M, N, K, ws, parts, M * 5 + N * 3 + K, f"halves {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,want", [(300, 700, 5120, 4), (1024, 1024, 5120, 4), (700, 1500, 6400, 4),
+                                        (512, 512, 12288, 8), (257, 300, 10240, 8), (33, 2000, 8160, 4),
+                                        (1, 300, 7424, 4), (300, 700, 4000, 2)])
+def test_split_many_parts(M, N, K, want):
+    """Longer K: four and eight parts per tile (ragged M, N and K; K steps that do
+    not divide evenly among the parts; one row); three parts' worth of K runs in
+    two."""
+    say(f"[mx gemm split {want} parts] {M}x{N}x{K}")
+    ws, parts = workspace_for(M, N, K)
+    if cus() == 256:
+        assert parts == want
+    run_case(M, N, K, ws, parts, M * 11 + N * 7 + K, f"{parts} parts {M}x{N}x{K}")
 
 
 def test_split_calls_in_a_row_share_the_workspace():
@@ -87,7 +111,7 @@ def test_split_calls_in_a_row_share_the_workspace():
     ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     for i, (M, N, K) in enumerate(shapes):
         say(f"[mx gemm split, shared workspace] call {i}: {M}x{N}x{K}")
-        run_case(M, N, K, ws, 100 + i, f"shared workspace call {i}")
+        run_case(M, N, K, ws, parts_expected(M, N, K), 100 + i, f"shared workspace call {i}")
 
 
 def test_split_unsplit_when_no_workspace_or_nothing_to_split():
@@ -123,9 +147,9 @@ def test_split_workspace_too_small_is_rejected():
 
 def test_split_flux_down_projection_1024_tokens():
     """FLUX MLP down-projection for 1024 tokens (1024 x 3072 x 12288: 48 tiles of
-    48 K steps, 96 workgroups), on the quantizer's own outputs: every fp32 output
-    against the reference, and bf16 (the LDS-staged path) equal to the rounded
-    fp32."""
+    48 K steps, in four parts on 192 workgroups), on the quantizer's own outputs:
+    every fp32 output against the reference, and bf16 (the LDS-staged path) equal
+    to the rounded fp32."""
     import torch
     cfg, wcfg = synth.get_config("flux_mlp"), synth.get_weight_config("flux_w_down")
     say("[mx gemm split full size] 1024 x 3072 x 12288, every output")
@@ -135,12 +159,12 @@ def test_split_flux_down_projection_1024_tokens():
     qx, sx = kq.kq_quantize(dev(x), pd)
     qw, sw = kq.kq_quantize_weights(dev(w), pd)
     M, N, K = 1024, wcfg.rows, cfg.d
-    ws, split = workspace_for(M, N, K)
-    assert split
+    ws, parts = workspace_for(M, N, K)
+    assert parts >= 2
     y32 = kq.kq_mx_gemm_ws(qx, sx, qw, sw, ws)
     y16 = kq.kq_mx_gemm_ws(qx, sx, qw, sw, ws, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(y32.to(torch.bfloat16), y16)
     assert int(ws[:FLAG_BYTES].count_nonzero()) == 0
     Yref, Yabs = oracle.mx_gemm(host(qx), host(sx), host(qw), host(sw))
-    check(host(y32), Yref, Yabs, K, "split 1024 x 3072 x 12288")
+    check(host(y32), Yref, Yabs, K, f"split 1024 x 3072 x 12288 ({parts} parts)", parts=parts)

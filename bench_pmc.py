@@ -134,7 +134,12 @@ TRACE_KERNELS = [
      "`butterfly_kernel<bf16, -, weights>` (kq_quantize_weights, 12288x3072)"),
     ("gemm unsplit 216", "`mx_gemm_kernel<256x256 tiles, bf16 out, staged>` (kq_mx_gemm, 4608x12288x3072, 216 workgroups)"),
     ("gemm unsplit 48", "`mx_gemm_kernel<256x256 tiles, bf16 out, staged>` (kq_mx_gemm, 1024x3072x12288, 48 workgroups)"),
-    ("gemm split 96", "`mx_gemm_kernel<..., split>` (kq_mx_gemm_ws, 1024x3072x12288 in K halves, 96 workgroups)"),
+    ("gemm unsplit 18", "`mx_gemm_kernel<256x256 tiles, bf16 out, staged>` (kq_mx_gemm, 4608x256x3072, 18 workgroups)"),
+    ("fused gemm 256", "`fused_gemm_kernel` (kq_mx_gemm_fused, 4608x12288x3072, 256 workgroups)"),
+    ("fused gemm 36", "`fused_gemm_kernel` (kq_mx_gemm_fused, 4608x256x3072, 36 workgroups)"),
+    ("gemm split 192", "`mx_gemm_kernel<..., split>` (kq_mx_gemm_ws, 1024x3072x12288 in 4 K parts, 192 workgroups)"),
+    ("gemm split 96",
+     "`mx_gemm_kernel<..., split>` (kq_mx_gemm_static, 1024x3072x12288 in 2 K parts, 96 workgroups)"),
     ("mlp-shape void kq::(anonymous namespace)::butterfly_kernel<0, false, 0>",
      "`butterfly_kernel<bf16, -, forward>` on 4608x12288 (the last leg)"),
     ("void at::native::(anonymous namespace)::vectorized_layer_norm_kernel", "torch layer_norm (unfused sequence)"),
@@ -163,6 +168,8 @@ def trace(trace_dir, bench_json):
             # the grid (workgroups of 512 lanes) tells the two unsplit shapes apart
             grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0) // 512
             name = f"gemm {'split' if name.split('>(')[0].endswith('true') else 'unsplit'} {grid}"
+        elif "fused_gemm_kernel<" in name:
+            name = f"fused gemm {int(r.get('Grid_Size_X') or r.get('Grid_Size') or 0) // 512}"
         dur.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
     b = json.load(open(bench_json))
 

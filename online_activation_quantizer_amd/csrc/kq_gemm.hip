@@ -562,8 +562,8 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   // accumulation starts at +0).  Other slot k is part k, or k + 1 from this part
   // on.
   auto all_parts_n = [&](auto no_c) {
+    constexpr int NO = decltype(no_c)::value;
     return [&](int i, int j, int q, const f32x4& own) {
-      constexpr int NO = decltype(no_c)::value;
       const int piece = 16 * kThreads * ((i * T::kTN + j) * 4 + q);
       f32x4 x[NO];
 #pragma unroll

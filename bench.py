@@ -580,9 +580,12 @@ def gemm_split_timing(args):
 def gemm_fused_timing(args):
     """The product with the quantizer in its prologue (kq_mx_gemm_fused: bf16 X and
     the factor parameters in, no MXFP4 activation operand in memory) beside the
-    unfused pair (kq_quantize, then kq_mx_gemm, in one graph) on the FLUX.1-schnell
+    unfused pair (kq_quantize, then the product, in one graph) on the FLUX.1-schnell
     MLP up-projection, and on its first 256 weight rows (one tile column of Y, the
-    case where the fused path quantizes each activation tile only once)."""
+    case where the fused path quantizes each activation tile only once).  Both
+    products run through their workspace entries (kq_mx_gemm_fused_ws and
+    kq_mx_gemm_ws), which split few tiles in K parts; "fused_whole" is the fused
+    product without a workspace."""
     import torch
 
     import synth
@@ -601,14 +604,19 @@ def gemm_fused_timing(args):
     for N in (wcfg.rows, 256):
         qb, sb = qw[:N], sw[:N]
         out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        nf, nu = kq.kq_mx_gemm_fused_workspace_size(M, N, K), kq.kq_mx_gemm_workspace_size(M, N, K)
+        wsf = torch.zeros(max(nf, 4096), dtype=torch.uint8, device="cuda")
+        wsu = torch.zeros(max(nu, 4096), dtype=torch.uint8, device="cuda")
         legs = {}
-        for name, fn in (("fused", lambda i: kq.kq_mx_gemm_fused(xd, pd, qb, sb, out=out)),
+        for name, fn in (("fused", lambda i: kq.kq_mx_gemm_fused_ws(xd, pd, qb, sb, wsf, out=out)),
+                         ("fused_whole", lambda i: kq.kq_mx_gemm_fused(xd, pd, qb, sb, out=out)),
                          ("quantize_then_product", lambda i: (kq.kq_quantize(xd, pd, q=q, s=s),
-                                                              kq.kq_mx_gemm(q, s, qb, sb, out=out)))):
+                                                              kq.kq_mx_gemm_ws(q, s, qb, sb, wsu, out=out)))):
             ms = (timed(fn, steps, args.warmup, torch.cuda.current_stream()) if args.eager
                   else timed_graph(fn, steps, min(args.warmup, 10)))
             legs[name] = {"ms_per_call": round(ms, 6),
                           "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+        legs["workspace_bytes"] = {"fused": nf, "product": nu}
         legs["t_fused_over_t_unfused"] = round(legs["fused"]["ms_per_call"] /
                                                legs["quantize_then_product"]["ms_per_call"], 4)
         res[f"n{N}"] = legs

@@ -246,6 +246,37 @@ int kq_mx_gemm_fused(const void* x, int dtype, int64_t ldx, const float* params,
                      const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
                      int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream);
 
+/* Bytes of device workspace that kq_mx_gemm_fused_ws uses for an M x N x K product
+ * on the current device (written to *bytes; 0 when nothing is split, which is then
+ * the same product as kq_mx_gemm_fused).  The fused product computes 128 x 256
+ * output tiles, at most one workgroup per compute unit, and each tile quantizes its
+ * activation rows over all of K, so with few tiles the quantization runs on few
+ * compute units.  When twice the tiles (rounded up to a multiple of 8) fit on the
+ * compute units and K has at least 6 steps of 256, each tile is computed as S
+ * parts of K on S compute units of one XCD (each quantizing and multiplying its K
+ * steps only), which meet through the workspace: S is the largest of 2, 4 and 8
+ * such that S times the tiles (rounded up to 8) fit on the compute units and every
+ * part has at least 3 K steps.  The workspace is 4096 bytes of flag words, then
+ * S x 128 KiB of fp32 partial sums per tile; the parts' sums are added in part
+ * order.
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_HIP. */
+int kq_mx_gemm_fused_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes);
+
+/* kq_mx_gemm_fused with a caller-owned device workspace (same arguments, and the
+ * result up to the fp32 rounding of the parts' sums, within the product's bound):
+ *   workspace        device memory, 256-byte aligned (KQ_ERR_ALIGN), of at least
+ *                    kq_mx_gemm_fused_workspace_size bytes (KQ_ERR_VALUE); its first
+ *                    4096 bytes are zero before the first call, and every call
+ *                    leaves them zero.  NULL with workspace_bytes 0: no split, as
+ *                    kq_mx_gemm_fused (NULL with other sizes: KQ_ERR_NULL).
+ * Calls that share a workspace must not run at the same time (one stream, or
+ * ordered streams).  The library allocates nothing.
+ * Errors: as kq_mx_gemm_fused, and KQ_ERR_VALUE. */
+int kq_mx_gemm_fused_ws(const void* x, int dtype, int64_t ldx, const float* params,
+                        const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+                        int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* workspace,
+                        int64_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace that kq_mx_gemm_ws uses for an M x N x K product on
  * the current device (written to *bytes; 0 when nothing is split, which is then
  * the same product as kq_mx_gemm).  The product computes 256 x 256 output tiles, at

@@ -10,6 +10,7 @@ from .kq import (  # noqa: F401
     sq_quantize, sq_transform_debug, expanded_numel, EXPORTED_SYMBOLS, kq_quantize_weights,
     kq_weights_debug, hq_quantize, hq_transform_debug, kq_norm_quantize, kq_norm_debug, kq_mx_gemm,
     kq_mx_gemm_workspace_size, kq_mx_gemm_ws, kq_mx_gemm_static, kq_mx_gemm_fused,
+    kq_mx_gemm_fused_ws, kq_mx_gemm_fused_workspace_size,
     KQ_OK, KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_DTYPE, KQ_ERR_FORMAT, KQ_ERR_VARIANT,
     KQ_ERR_HIP, KQ_ERR_VALUE, KQ_ERR_DEVICE,
 )

@@ -250,6 +250,35 @@ int mx_gemm_impl(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa
   return e == hipSuccess ? KQ_OK : fail_hip(e);
 }
 
+int mx_gemm_fused_impl(const void* x, int dtype, int64_t ldx, const float* params, const uint8_t* qb,
+                       int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M, int64_t N, int64_t K,
+                       void* out, int64_t ldo, int out_dtype, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
+  if (dtype != KQ_BF16) return KQ_ERR_DTYPE;  // the prologue reads bf16 activations only
+  if (out_dtype != KQ_FP32 && out_dtype != KQ_BF16) return KQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || K / 32 > kq::kFusedMaxBlocks || M > kMaxRows ||
+      N > kMaxRows || ldx < K || ldb < K / 2 || ldsb < K / 32 || ldo < N || ldx * 2 > kMaxPitch ||
+      ldb > kMaxPitch || ldsb > kMaxPitch || ldo * (out_dtype == KQ_FP32 ? 4 : 2) > kMaxPitch)
+    return KQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return KQ_OK;
+  if (!x || !params || !qb || !sb || !out) return KQ_ERR_NULL;
+  if (!aligned(x, 16) || (ldx * 2) % 16 != 0 || !aligned(qb, 16) || ldb % 16 != 0 ||
+      !aligned(out, out_dtype == KQ_FP32 ? 4 : 2))
+    return KQ_ERR_ALIGN;
+  if (!workspace && workspace_bytes != 0) return KQ_ERR_NULL;
+  if (workspace && !aligned(workspace, 256)) return KQ_ERR_ALIGN;
+  int cus = 0;
+  const int rc = current_cus(&cus);
+  if (rc != KQ_OK) return rc;
+  if (workspace && workspace_bytes < kq::mx_gemm_fused_workspace_bytes(M, N, K, cus)) return KQ_ERR_VALUE;
+  kq::FusedGemmArgs g{x, ldx, params, qb, ldb, sb, ldsb, M, N, K, out, ldo,
+                      out_dtype == KQ_BF16, stream, cus};
+  g.workspace = workspace;
+  g.workspace_bytes = workspace_bytes;
+  const hipError_t e = kq::launch_mx_gemm_fused(g);
+  return e == hipSuccess ? KQ_OK : fail_hip(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -341,24 +370,30 @@ int kq_mx_gemm(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t ldsa,
 int kq_mx_gemm_fused(const void* x, int dtype, int64_t ldx, const float* params,
                      const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
                      int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* stream) {
-  if (dtype != KQ_BF16) return KQ_ERR_DTYPE;  // the prologue reads bf16 activations only
-  if (out_dtype != KQ_FP32 && out_dtype != KQ_BF16) return KQ_ERR_DTYPE;
+  return mx_gemm_fused_impl(x, dtype, ldx, params, qb, ldb, sb, ldsb, M, N, K, out, ldo, out_dtype, nullptr, 0,
+                            stream);
+}
+
+int kq_mx_gemm_fused_ws(const void* x, int dtype, int64_t ldx, const float* params,
+                        const uint8_t* qb, int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t M,
+                        int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
+  return mx_gemm_fused_impl(x, dtype, ldx, params, qb, ldb, sb, ldsb, M, N, K, out, ldo, out_dtype, workspace,
+                            workspace_bytes, stream);
+}
+
+int kq_mx_gemm_fused_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes) {
+  if (!bytes) return KQ_ERR_NULL;
+  *bytes = 0;
   if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || K / 32 > kq::kFusedMaxBlocks || M > kMaxRows ||
-      N > kMaxRows || ldx < K || ldb < K / 2 || ldsb < K / 32 || ldo < N || ldx * 2 > kMaxPitch ||
-      ldb > kMaxPitch || ldsb > kMaxPitch || ldo * (out_dtype == KQ_FP32 ? 4 : 2) > kMaxPitch)
+      N > kMaxRows)
     return KQ_ERR_SHAPE;
   if (M == 0 || N == 0) return KQ_OK;
-  if (!x || !params || !qb || !sb || !out) return KQ_ERR_NULL;
-  if (!aligned(x, 16) || (ldx * 2) % 16 != 0 || !aligned(qb, 16) || ldb % 16 != 0 ||
-      !aligned(out, out_dtype == KQ_FP32 ? 4 : 2))
-    return KQ_ERR_ALIGN;
   int cus = 0;
   const int rc = current_cus(&cus);
   if (rc != KQ_OK) return rc;
-  const kq::FusedGemmArgs g{x, ldx, params, qb, ldb, sb, ldsb, M, N, K, out, ldo,
-                            out_dtype == KQ_BF16, stream, cus};
-  const hipError_t e = kq::launch_mx_gemm_fused(g);
-  return e == hipSuccess ? KQ_OK : fail_hip(e);
+  *bytes = kq::mx_gemm_fused_workspace_bytes(M, N, K, cus);
+  return KQ_OK;
 }
 
 int kq_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes) {

@@ -43,6 +43,7 @@
 #include <type_traits>
 
 #include "kq_launch.hpp"
+#include "kq_split.hpp"
 
 namespace kq {
 namespace {
@@ -497,33 +498,21 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
   }
   if constexpr (!SPLIT) return;
 
-  // The parts of a split tile meet through its flag word and one fp32 tile of
+  // The parts of a split tile meet through its flag word and one fp32 slot of
   // partial sums per part (thread tid's accumulators as 16-byte pieces, piece c at
-  // c kThreads + tid).  Each part adds 1 to the flag on arrival (bits 0-7 count
-  // the arrivals).  Every part but the last to arrive stores its sums in its own
-  // slot, waits until they are visible to the device and adds kReady (bits 8-15
-  // count the stored parts); the last waits for parts - 1 stored parts, which come
-  // from workgroups already running that wait for nothing, adds every part's sums
-  // in part order (its own from registers), so the result does not depend on the
-  // order of arrival, puts the flag back to 0 for the next call and writes the
-  // tile.  No workgroup waits for one that may not have started, whatever the
-  // order workgroups run in.
-  constexpr uint32_t kReady = 256u;
+  // c kThreads + tid; the exchange itself in kq_split.hpp).  The last part adds
+  // every part's sums in part order (its own from registers), so the result does
+  // not depend on the order of arrival.
   __shared__ uint32_t arrival;
   uint32_t* flag = flags + h_tile;
   // the tile's part slots through one buffer descriptor: piece c of part p's slot
   // for this thread at byte offset 16 tid (per lane) + 16 kThreads c + p x tile
-  // bytes (per instruction).  They are stored and loaded device-coherent (cache
-  // policy sc1, the form of agent-scope relaxed atomics), so they need no cache
-  // write-back or invalidation, which would also drop the other workgroups'
-  // operands from the XCD's L2.
+  // bytes (per instruction)
   constexpr int kTileBytes = kBM * T::kBN * 4;
   const __amdgpu_buffer_rsrc_t rsrc_p = __builtin_amdgcn_make_buffer_rsrc(
       partials + (uint64_t)h_tile * parts * (kBM * T::kBN), 0, (int)(parts * (uint32_t)kTileBytes), 0x00020000);
-  constexpr int kDeviceCoherent = 16;  // sc1
-  if (tid == 0) arrival = __hip_atomic_fetch_add(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if ((__builtin_amdgcn_readfirstlane(arrival) & 0xFFu) + 1u < parts) {
+  constexpr int kDeviceCoherent = kSplitCoherent;
+  if (!split_arrive_last(flag, parts, arrival)) {
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i)
 #pragma unroll
@@ -536,24 +525,10 @@ __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(2))
                                                      16 * kThreads * ((i * T::kTN + j) * 4 + q),
                                                  kDeviceCoherent);
         }
-    // every wave's stores complete (visible device-wide) before the flag changes
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#endif
-    __syncthreads();
-    if (tid == 0) __hip_atomic_fetch_add(flag, kReady, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    split_publish(flag);
     return;
   }
-  if (tid == 0) {
-    // bounded: the other parts have arrived and only store their sums before kReady
-    for (uint32_t n = 0; n < (1u << 26); ++n) {
-      if (((__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 8) & 0xFFu) + 1u >= parts)
-        break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
-  __syncthreads();
-  if (tid == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  split_wait_reset(flag, parts);
   // The tile's sums, parts 0, 1, ... added in that order (the order of arrival
   // does not matter).  The other parts' slots are loaded branch-free, NO of them
   // per piece, NO = 1, 3 or 7 (the schedule makes it parts - 1; were it more, the

@@ -95,9 +95,16 @@ struct FusedGemmArgs {
   bool out_bf16;
   void* stream;
   int cus;
+  // device workspace for tiles split in K parts (flags first, zero between calls),
+  // or NULL for whole tiles only; tiles are split only as far as it holds their
+  // parts (all of mx_gemm_fused_workspace_bytes() when it holds that much)
+  void* workspace = nullptr;
+  int64_t workspace_bytes = 0;
 };
 // Every block's transform constants sit in the fused product's LDS: K <= 32 x this.
 constexpr int64_t kFusedMaxBlocks = 512;
+// One slot of a split 128 x 256 output tile's fp32 partial sums.
+constexpr int64_t kFusedSplitTileBytes = 128 * 256 * 4;
 
 inline int64_t gcd64(int64_t a, int64_t b) {
   while (b) {
@@ -130,6 +137,8 @@ hipError_t launch_hadamard(const LaunchArgs& a);  // fixed block-Hadamard, then 
 hipError_t launch_norm(const NormArgs& n);        // LayerNorm + modulation, T_b, MXFP4
 hipError_t launch_mx_gemm(const GemmArgs& g);    // Y = deq(A) deq(B)^T on scaled MFMA
 hipError_t launch_mx_gemm_fused(const FusedGemmArgs& g);  // Y = deq(Q(T X)) deq(B)^T
+// Workspace bytes of the fused product's split schedule (0 if its tiles are not split).
+int64_t mx_gemm_fused_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus);
 // Workspace bytes of the split schedule of an M x N x K product on `cus` compute
 // units whose workspace holds at most max_slots partial-sum slots (0 if its tiles
 // are not split).

@@ -34,7 +34,7 @@ EXPORTED_SYMBOLS = ("kq_expand_factors", "kq_quantize", "sq_quantize", "kq_trans
                     "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug",
                     "hq_quantize", "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug",
                     "kq_mx_gemm", "kq_mx_gemm_fused", "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws",
-                    "kq_mx_gemm_static",
+                    "kq_mx_gemm_static", "kq_mx_gemm_fused_workspace_size", "kq_mx_gemm_fused_ws",
                     "kq_status_string", "kq_last_hip_error")
 
 
@@ -75,6 +75,8 @@ def lib():
         L.kq_mx_gemm_ws.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, I64, I, P, I64, P]
         L.kq_mx_gemm_static.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, I64, I, P]
         L.kq_mx_gemm_fused.argtypes = [P, I, I64, P, P, I64, P, I64, I64, I64, I64, P, I64, I, P]
+        L.kq_mx_gemm_fused_workspace_size.argtypes = [I64, I64, I64, ctypes.POINTER(I64)]
+        L.kq_mx_gemm_fused_ws.argtypes = [P, I, I64, P, P, I64, P, I64, I64, I64, I64, P, I64, I, P, I64, P]
         L.kq_status_string.argtypes = [I]
         L.kq_status_string.restype = ctypes.c_char_p
         L.kq_last_hip_error.argtypes = []
@@ -440,8 +442,28 @@ def kq_mx_gemm_fused(x, params, qb, sb, out=None, out_dtype=None, stream=None):
     deq(B)^T from bf16 x [M, K], its float32 factor parameters [K/32, 5, 3] and the
     weights' MXFP4 operand (codes [N, K/2], scales [N, K/32]); equal to
     kq_mx_gemm(*kq_quantize(x, params), qb, sb) bit for bit."""
+    return _mx_gemm_fused("kq_mx_gemm_fused", x, params, qb, sb, out, out_dtype, False, stream)
+
+
+def kq_mx_gemm_fused_ws(x, params, qb, sb, workspace, out=None, out_dtype=None, stream=None):
+    """kq_mx_gemm_fused with each 128 x 256 output tile split into 2, 4 or 8 parts
+    of K through ``workspace`` when the library's rule splits the shape (uint8
+    device tensor of kq_mx_gemm_fused_workspace_size bytes whose first 4096 bytes
+    are zero before the first call; every call leaves them zero).
+    ``workspace=None`` runs the unsplit product."""
+    return _mx_gemm_fused("kq_mx_gemm_fused_ws", x, params, qb, sb, out, out_dtype, workspace, stream)
+
+
+def kq_mx_gemm_fused_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace kq_mx_gemm_fused_ws uses for an M x N x K product on the
+    current device."""
+    n = ctypes.c_int64(0)
+    _check(lib().kq_mx_gemm_fused_workspace_size(M, N, K, ctypes.byref(n)), "kq_mx_gemm_fused_workspace_size")
+    return n.value
+
+
+def _mx_gemm_fused(what, x, params, qb, sb, out, out_dtype, workspace, stream):
     import torch
-    what = "kq_mx_gemm_fused"
     _need_input(what, x)
     if _dtype_code(x) != KQ_BF16:
         _fail(KQ_ERR_DTYPE, f"{what}: x must be bf16, got {x.dtype}")
@@ -466,10 +488,20 @@ def kq_mx_gemm_fused(x, params, qb, sb, out=None, out_dtype=None, stream=None):
     if out.dim() != 2 or tuple(out.shape) != (M, N):
         _fail(KQ_ERR_SHAPE, f"{what}: out is {tuple(out.shape)}, needs ({M}, {N})")
     _row_pitch(out)
-    _need_device(what, x, params=params, qb=qb, sb=sb, out=out)
-    _check(lib().kq_mx_gemm_fused(x.data_ptr(), KQ_BF16, _row_pitch(x), params.data_ptr(), qb.data_ptr(),
-                                  _row_pitch(qb), sb.data_ptr(), _row_pitch(sb), M, N, K, out.data_ptr(),
-                                  _row_pitch(out), code, _stream(stream)), what)
+    args = (x.data_ptr(), KQ_BF16, _row_pitch(x), params.data_ptr(), qb.data_ptr(), _row_pitch(qb),
+            sb.data_ptr(), _row_pitch(sb), M, N, K, out.data_ptr(), _row_pitch(out), code)
+    if workspace is False:
+        _need_device(what, x, params=params, qb=qb, sb=sb, out=out)
+        _check(lib().kq_mx_gemm_fused(*args, _stream(stream)), what)
+        return out
+    if workspace is None:
+        _need_device(what, x, params=params, qb=qb, sb=sb, out=out)
+        _check(lib().kq_mx_gemm_fused_ws(*args, None, 0, _stream(stream)), what)
+        return out
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
+        _fail(KQ_ERR_DTYPE, f"{what}: workspace must be a contiguous 1-D uint8 tensor")
+    _need_device(what, x, params=params, qb=qb, sb=sb, out=out, workspace=workspace)
+    _check(lib().kq_mx_gemm_fused_ws(*args, workspace.data_ptr(), workspace.numel(), _stream(stream)), what)
     return out
 
 

@@ -13,6 +13,9 @@ hipError_t launch_hadamard(const LaunchArgs&) { return hipErrorNotSupported; }
 hipError_t launch_norm(const NormArgs&) { return hipErrorNotSupported; }
 hipError_t launch_mx_gemm(const GemmArgs&) { return hipErrorNotSupported; }
 hipError_t launch_mx_gemm_fused(const FusedGemmArgs&) { return hipErrorNotSupported; }
+int64_t mx_gemm_fused_workspace_bytes(int64_t, int64_t, int64_t, int) {
+  return kSplitFlagBytes + kFusedSplitTileBytes;
+}
 int64_t mx_gemm_workspace_bytes(int64_t, int64_t, int64_t, int, int64_t) { return kSplitFlagBytes + kSplitTileBytes; }
 hipError_t static_scratch(void**, void*) { return hipErrorNotSupported; }
 hipError_t launch_sq(const LaunchArgs&) { return hipErrorNotSupported; }

@@ -30,7 +30,7 @@ def test_header_symbols_exported(L):
             "sq_transform_debug", "kq_quantize_weights", "kq_weights_debug", "hq_quantize",
             "hq_transform_debug", "kq_norm_quantize", "kq_norm_debug", "kq_mx_gemm",
             "kq_mx_gemm_workspace_size", "kq_mx_gemm_ws", "kq_mx_gemm_static", "kq_mx_gemm_fused",
-            "kq_status_string",
+            "kq_mx_gemm_fused_workspace_size", "kq_mx_gemm_fused_ws", "kq_status_string",
             "kq_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -195,6 +195,27 @@ def test_mx_gemm_fused_validation(L):
     assert g(x=X + 8) == ALIGN
     assert g(ldx=132) == ALIGN                   # 264-byte rows
     assert g(M=0, x=None, p=None, qb=None, sb=None, out=None) == OK
+
+
+def test_mx_gemm_fused_workspace_validation(L):
+    W = 0x60000
+
+    def g(ws=W, nbytes=1 << 20, **kw):
+        a = dict(x=X, dt=0, ldx=128, p=T, qb=Q, ldb=64, sb=S, ldsb=4, M=8, N=8, K=128, out=Y, ldo=8, odt=1)
+        a.update(kw)
+        return L.kq_mx_gemm_fused_ws(a["x"], a["dt"], a["ldx"], a["p"], a["qb"], a["ldb"], a["sb"], a["ldsb"],
+                                     a["M"], a["N"], a["K"], a["out"], a["ldo"], a["odt"], ws, nbytes, None)
+    assert g(dt=1) == DTYPE                      # the fused product's own checks come first
+    assert g(K=48, ldb=32) == SHAPE
+    assert g(p=None) == NULL
+    assert g(ws=None, nbytes=4096) == NULL       # a size without a workspace
+    assert g(ws=W + 128) == ALIGN                # 256-byte alignment
+    assert g(M=0, ws=None, nbytes=0, x=None, p=None, qb=None, sb=None, out=None) == OK
+    n = ctypes.c_int64(-1)
+    assert L.kq_mx_gemm_fused_workspace_size(8, 8, 128, None) == NULL
+    assert L.kq_mx_gemm_fused_workspace_size(8, 8, 48, ctypes.byref(n)) == SHAPE
+    assert L.kq_mx_gemm_fused_workspace_size(8, 8, 16416, ctypes.byref(n)) == SHAPE  # past the on-chip constants
+    assert L.kq_mx_gemm_fused_workspace_size(0, 8, 128, ctypes.byref(n)) == OK and n.value == 0
 
 
 def test_mx_gemm_workspace_validation(L):

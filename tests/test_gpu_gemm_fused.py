@@ -84,6 +84,82 @@ def test_fused_flux_mlp_full_size():
         oracle_rows=np.sort(np.random.default_rng(1).choice(4608, 256, replace=False)))
 
 
+FLAG_BYTES = 4096
+FUSED_TILE_BYTES = 128 * 256 * 4
+FUSED_MIN_STEPS_PER_PART = 3
+
+
+def fused_parts_expected(M, N, K):
+    """The rule the library states for the fused product's 128 x 256 tiles: the
+    largest of 2, 4 and 8 parts with that many times the tiles (rounded up to 8) on
+    the compute units (one workgroup each) and at least 3 K steps per part."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    full = max(8, cus // 8 * 8)
+    tiles = ((M + 127) // 128) * ((N + 255) // 256)
+    n8 = (tiles + 7) // 8 * 8
+    p = min(full // n8, ((K + 255) // 256) // FUSED_MIN_STEPS_PER_PART)
+    p = 8 if p >= 8 else 4 if p >= 4 else 2 if p >= 2 else p
+    return (p if p >= 2 and tiles <= FLAG_BYTES // 4 else 1), tiles
+
+
+@pytest.mark.parametrize("M,N,K,want", [(4608, 256, 3072, 4), (1000, 300, 4096, 4), (300, 256, 8192, 8),
+                                        (129, 600, 2400, 2), (64, 1030, 1600, 2)])
+def test_fused_split(M, N, K, want):
+    """Few tiles: each 128 x 256 tile in K parts through a workspace (the FLUX MLP
+    up-projection's first 256 weight rows; ragged M, N and K; N = 1030 takes the
+    one-output-per-store path).  Against the oracle chain on the GPU's codes within
+    the product's bound with one rounding per part, bf16 equal to the rounded fp32,
+    the flags left at zero, and the unsplit fused product within the same bound."""
+    import torch
+    parts, tiles = fused_parts_expected(M, N, K)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert parts == want
+    n = kq.kq_mx_gemm_fused_workspace_size(M, N, K)
+    assert n == (FLAG_BYTES + parts * tiles * FUSED_TILE_BYTES if parts > 1 else 0), (n, parts, tiles)
+    ws = torch.zeros(max(n, FLAG_BYTES), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(M + N * 3 + K * 7)
+    x, p = activations(M, K, rng)
+    qb, sb = random_mx(N, K, rng)
+    xd, pd, qbd, sbd = dev(x), dev(p), dev(qb), dev(sb)
+    say(f"[mx gemm fused split] {M}x{N}x{K}, {parts} parts")
+    y32 = kq.kq_mx_gemm_fused_ws(xd, pd, qbd, sbd, ws)
+    y16 = kq.kq_mx_gemm_fused_ws(xd, pd, qbd, sbd, ws, out_dtype=torch.bfloat16)
+    whole = kq.kq_mx_gemm_fused(xd, pd, qbd, sbd)
+    qa, sa = kq.kq_quantize(xd, pd)
+    torch.cuda.synchronize()
+    assert torch.equal(y32.to(torch.bfloat16), y16)
+    assert int(ws[:FLAG_BYTES].count_nonzero()) == 0
+    Yref, Yabs = oracle.mx_gemm(host(qa), host(sa), qb, sb)
+    check(host(y32), Yref, Yabs, K, f"split {M}x{N}x{K} (GPU codes)", parts=max(2, parts))
+    check(host(whole), Yref, Yabs, K, f"unsplit {M}x{N}x{K} (GPU codes)")
+
+
+def test_fused_split_calls_in_a_row_and_no_workspace():
+    """Two split calls in a row on one workspace, the second smaller; no workspace:
+    the unsplit fused product, bit for bit."""
+    import torch
+    shapes = [(1000, 300, 4096), (300, 256, 8192)]
+    n = max(kq.kq_mx_gemm_fused_workspace_size(*sh) for sh in shapes)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    for i, (M, N, K) in enumerate(shapes):
+        rng = np.random.default_rng(50 + i)
+        x, p = activations(M, K, rng)
+        qb, sb = random_mx(N, K, rng)
+        xd, pd, qbd, sbd = dev(x), dev(p), dev(qb), dev(sb)
+        y = kq.kq_mx_gemm_fused_ws(xd, pd, qbd, sbd, ws)
+        qa, sa = kq.kq_quantize(xd, pd)
+        torch.cuda.synchronize()
+        assert int(ws[:FLAG_BYTES].count_nonzero()) == 0
+        Yref, Yabs = oracle.mx_gemm(host(qa), host(sa), qb, sb)
+        check(host(y), Yref, Yabs, K, f"shared workspace call {i}", parts=8)
+        if i == 0:
+            a = kq.kq_mx_gemm_fused_ws(xd, pd, qbd, sbd, None)
+            b = kq.kq_mx_gemm_fused(xd, pd, qbd, sbd)
+            torch.cuda.synchronize()
+            assert torch.equal(a, b)
+
+
 def test_fused_rejects():
     import torch
     x = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")

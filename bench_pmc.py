@@ -134,9 +134,10 @@ TRACE_KERNELS = [
      "`butterfly_kernel<bf16, -, weights>` (kq_quantize_weights, 12288x3072)"),
     ("gemm unsplit 216", "`mx_gemm_kernel<256x256 tiles, bf16 out, staged>` (kq_mx_gemm, 4608x12288x3072, 216 workgroups)"),
     ("gemm unsplit 48", "`mx_gemm_kernel<256x256 tiles, bf16 out, staged>` (kq_mx_gemm, 1024x3072x12288, 48 workgroups)"),
-    ("gemm unsplit 18", "`mx_gemm_kernel<256x256 tiles, bf16 out, staged>` (kq_mx_gemm, 4608x256x3072, 18 workgroups)"),
+    ("gemm split 48", "`mx_gemm_kernel<..., split>` (kq_mx_gemm_ws, 4608x256x3072 in 2 K parts, 48 workgroups)"),
     ("fused gemm 256", "`fused_gemm_kernel` (kq_mx_gemm_fused, 4608x12288x3072, 256 workgroups)"),
-    ("fused gemm 36", "`fused_gemm_kernel` (kq_mx_gemm_fused, 4608x256x3072, 36 workgroups)"),
+    ("fused gemm 36", "`fused_gemm_kernel` (kq_mx_gemm_fused, 4608x256x3072 whole tiles, 36 workgroups)"),
+    ("fused gemm 160", "`fused_gemm_kernel<..., split>` (kq_mx_gemm_fused_ws, 4608x256x3072 in 4 K parts, 160 workgroups)"),
     ("gemm split 192", "`mx_gemm_kernel<..., split>` (kq_mx_gemm_ws, 1024x3072x12288 in 4 K parts, 192 workgroups)"),
     ("gemm split 96",
      "`mx_gemm_kernel<..., split>` (kq_mx_gemm_static, 1024x3072x12288 in 2 K parts, 96 workgroups)"),

@@ -175,3 +175,39 @@ def test_fused_rejects():
                             torch.zeros((1, 8208), dtype=torch.uint8, device="cuda"),
                             torch.zeros((1, 513), dtype=torch.uint8, device="cuda"))
     assert e.value.status == kq.KQ_ERR_SHAPE
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_fused_split_random_shapes_and_pitches(case):
+    """Seeded random shapes with few tiles (M in [1, 1200), N in [1, 700), K a
+    multiple of 32 in [768, 10240)), activation, weight and output pitches padded:
+    fp32 within the bound for the rule's part count against the oracle on the GPU's
+    codes (kq_quantize of the same pitched rows), bf16 the rounded fp32, nothing
+    written past N in a row, the flags left at zero."""
+    import torch
+    from test_gpu_gemm_split import pitched, sentinel_outputs, padding_untouched
+    rng = np.random.default_rng(4242 + case)
+    M, N, K = int(rng.integers(1, 1200)), int(rng.integers(1, 700)), 32 * int(rng.integers(24, 320))
+    px, pb, psb, po = 8 * int(rng.integers(0, 3)), 16 * int(rng.integers(0, 3)), int(rng.integers(0, 6)), \
+        int(rng.integers(0, 9))
+    parts, _ = fused_parts_expected(M, N, K)
+    say(f"[mx gemm fused split sweep {case}] {M}x{N}x{K}, {parts} parts, pads {px} {pb} {psb} {po}")
+    x, p = activations(M, K, rng)
+    qb, sb = random_mx(N, K, rng)
+    xw = torch.zeros((M, K + px), dtype=torch.int16, device="cuda")
+    xw[:, :K] = dev(x)
+    xd, pd = xw[:, :K], dev(p)
+    qbd, sbd = pitched(qb, pb, 0xA5), pitched(sb, psb, 0x88)
+    n = kq.kq_mx_gemm_fused_workspace_size(M, N, K)
+    ws = torch.zeros(max(n, FLAG_BYTES), dtype=torch.uint8, device="cuda") if n > 0 else None
+    o32, o16 = sentinel_outputs(M, N, po)
+    kq.kq_mx_gemm_fused_ws(xd, pd, qbd, sbd, ws, out=o32[:, :N])
+    kq.kq_mx_gemm_fused_ws(xd, pd, qbd, sbd, ws, out=o16[:, :N])
+    qa, sa = kq.kq_quantize(xd, pd)
+    torch.cuda.synchronize()
+    assert torch.equal(o32[:, :N].to(torch.bfloat16), o16[:, :N])
+    assert padding_untouched(o32, o16, N), "a store past N"
+    if ws is not None:
+        assert int(ws[:FLAG_BYTES].count_nonzero()) == 0
+    Yref, Yabs = oracle.mx_gemm(host(qa), host(sa), qb, sb)
+    check(host(o32[:, :N].contiguous()), Yref, Yabs, K, f"fused sweep {case}", parts=max(2, parts))

@@ -168,3 +168,74 @@ def test_split_flux_down_projection_1024_tokens():
     assert int(ws[:FLAG_BYTES].count_nonzero()) == 0
     Yref, Yabs = oracle.mx_gemm(host(qx), host(sx), host(qw), host(sw))
     check(host(y32), Yref, Yabs, K, f"split 1024 x 3072 x 12288 ({parts} parts)", parts=parts)
+
+
+def sweep_cases(n, seed=20261203):
+    """Seeded random shapes and pitches: M, N in [1, 1200), K a multiple of 32 in
+    [1536, 11520) (6-45 K steps, so 1, 2, 4 or 8 parts), code-row pitches padded by
+    0-32 bytes, scale pitches by 0-5 bytes (word-aligned or not), output pitches by
+    0-8 elements."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M, N = int(rng.integers(1, 1200)), int(rng.integers(1, 1200))
+        K = 32 * int(rng.integers(48, 360))
+        pads = (16 * int(rng.integers(0, 3)), int(rng.integers(0, 6)), 16 * int(rng.integers(0, 3)),
+                int(rng.integers(0, 6)), int(rng.integers(0, 9)))
+        out.append((M, N, K) + pads)
+    return out
+
+
+def pitched(a, extra, fill):
+    """The uint8 matrix a in the leading columns of a device buffer `extra` bytes
+    wider per row (the row pitch), the padding filled with `fill`: the view."""
+    import torch
+    rows, cols = a.shape
+    whole = torch.full((rows, cols + extra), fill, dtype=torch.uint8, device="cuda")
+    whole[:, :cols] = dev(a)
+    return whole[:, :cols]
+
+
+SENTINEL_F32, SENTINEL_BF16 = 0x7FC0DEAD, 0x7FAD  # NaN payloads no product writes
+
+
+def sentinel_outputs(M, N, extra):
+    """fp32 and bf16 output buffers of row pitch N + extra filled with NaN
+    sentinels, and their M x N views."""
+    import torch
+    o32 = torch.full((M, N + extra), SENTINEL_F32, dtype=torch.int32, device="cuda").view(torch.float32)
+    o16 = torch.full((M, N + extra), SENTINEL_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    return o32, o16
+
+
+def padding_untouched(o32, o16, N):
+    import torch
+    return (bool(torch.all(o32.view(torch.int32)[:, N:] == SENTINEL_F32))
+            and bool(torch.all(o16.view(torch.int16)[:, N:] == SENTINEL_BF16)))
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_split_random_shapes_and_pitches(case):
+    """Seeded random shapes, padded operand and output pitches: fp32 within the bound
+    for the part count the rule gives, bf16 the rounded fp32, nothing written past N
+    in a row, the flags left at zero."""
+    import torch
+    M, N, K, pa, psa, pb, psb, po = sweep_cases(10)[case]
+    parts = parts_expected(M, N, K)
+    say(f"[mx gemm split sweep {case}] {M}x{N}x{K}, {parts} parts, pads {pa} {psa} {pb} {psb} {po}")
+    rng = np.random.default_rng(1000 + case)
+    qa, sa = random_mx(M, K, rng)
+    qb, sb = random_mx(N, K, rng)
+    args = (pitched(qa, pa, 0x5A), pitched(sa, psa, 0x77), pitched(qb, pb, 0xA5), pitched(sb, psb, 0x88))
+    n = kq.kq_mx_gemm_workspace_size(M, N, K)
+    ws = torch.zeros(max(n, FLAG_BYTES), dtype=torch.uint8, device="cuda") if n > 0 else None
+    o32, o16 = sentinel_outputs(M, N, po)
+    kq.kq_mx_gemm_ws(*args, ws, out=o32[:, :N])
+    kq.kq_mx_gemm_ws(*args, ws, out=o16[:, :N])
+    torch.cuda.synchronize()
+    assert torch.equal(o32[:, :N].to(torch.bfloat16), o16[:, :N])
+    assert padding_untouched(o32, o16, N), "a store past N"
+    if ws is not None:
+        assert int(ws[:FLAG_BYTES].count_nonzero()) == 0
+    Yref, Yabs = oracle.mx_gemm(qa, sa, qb, sb)
+    check(host(o32[:, :N].contiguous()), Yref, Yabs, K, f"sweep {case}", parts=max(2, parts))

@@ -136,7 +136,25 @@ int main() {
   EXPECT(kq_mx_gemm_fused(nullptr, 0, 128, nullptr, nullptr, 64, nullptr, 4, 0, 8, 128, nullptr, 8, 1,
                           nullptr),
          KQ_OK);
+  // the prologue-fused product with a workspace: the product's checks, then the
+  // workspace's own, all before any HIP call
+  EXPECT(kq_mx_gemm_fused_ws(X, 1, 128, P, Q, 64, S, 4, 8, 8, 128, Y, 8, 1, W, 1 << 20, nullptr), KQ_ERR_DTYPE);
+  EXPECT(kq_mx_gemm_fused_ws(X, 0, 128, P, Q, 64, S, 4, 8, 8, 48, Y, 8, 1, W, 1 << 20, nullptr), KQ_ERR_SHAPE);
+  EXPECT(kq_mx_gemm_fused_ws(X, 0, 128, P, Q, 64, S, 4, 8, 8, 128, Y, 8, 1, nullptr, 4096, nullptr),
+         KQ_ERR_NULL);
+  EXPECT(kq_mx_gemm_fused_ws(X, 0, 128, P, Q, 64, S, 4, 8, 8, 128, Y, 8, 1,
+                             reinterpret_cast<uint8_t*>(W) + 128, 1 << 20, nullptr),
+         KQ_ERR_ALIGN);
+  EXPECT(kq_mx_gemm_fused_ws(nullptr, 0, 128, nullptr, nullptr, 64, nullptr, 4, 0, 8, 128, nullptr, 8, 1, W, 0,
+                             nullptr),
+         KQ_OK);
   int64_t bytes = -1;
+  EXPECT(kq_mx_gemm_fused_workspace_size(8, 8, 128, nullptr), KQ_ERR_NULL);
+  EXPECT(kq_mx_gemm_fused_workspace_size(8, 8, 48, &bytes), KQ_ERR_SHAPE);
+  EXPECT(kq_mx_gemm_fused_workspace_size(8, 8, 16416, &bytes), KQ_ERR_SHAPE);
+  EXPECT(kq_mx_gemm_fused_workspace_size(0, 8, 128, &bytes), KQ_OK);
+  EXPECT((int)bytes, 0);
+  bytes = -1;
   EXPECT(kq_mx_gemm_workspace_size(8, 8, 128, nullptr), KQ_ERR_NULL);
   EXPECT(kq_mx_gemm_workspace_size(8, 8, 48, &bytes), KQ_ERR_SHAPE);
   EXPECT(kq_mx_gemm_workspace_size(-1, 8, 128, &bytes), KQ_ERR_SHAPE);

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     const uint8_t* __restrict__ x, uint32_t ldx, const float* __restrict__ params,
     const uint8_t* __restrict__ qb, uint32_t ldb, const uint8_t* __restrict__ sb, uint32_t ldsb,
     uint32_t M, uint32_t N, uint32_t K, void* __restrict__ out, uint32_t ldo, uint32_t tiles_n,
-    uint32_t ntiles, uint32_t parts, uint32_t* __restrict__ flags, float* __restrict__ partials) {
+    uint32_t ntiles, uint32_t band_rows, uint32_t parts, uint32_t* __restrict__ flags,
+    float* __restrict__ partials) {
   __shared__ __attribute__((aligned(16))) uint8_t codes[kFRows * kFPitch];
   __shared__ __attribute__((aligned(16))) uint8_t scale_bytes[kFRows * 8];  // 8 per row per step
   __shared__ __attribute__((aligned(16))) float consts[kFusedMaxBlocks * kFConstStride];
@@ -131,7 +132,10 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   };
 
   for (uint32_t t = t_begin; t < ntiles; t += t_stride) {
-    const uint32_t m0 = (t / tiles_n) * kFBM, n0 = (t % tiles_n) * kFBN;
+    // (split: each XCD's tiles as one compact block of the tile grid, split_tile)
+    uint32_t tm = t / tiles_n, tn = t - tm * tiles_n;
+    if constexpr (SPLIT) split_tile(t, ntiles, tiles_n, band_rows, tm, tn);
+    const uint32_t m0 = tm * kFBM, n0 = tn * kFBN;
     v16f acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -379,6 +383,7 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 constexpr int64_t kFusedMinStepsPerPart = 3;
 struct FusedSchedule {
   int64_t tiles_n, ntiles, grid, parts;
+  int64_t band_rows;  // split: tile rows per band of the compact per-XCD order
   bool split;
 };
 
@@ -400,6 +405,7 @@ FusedSchedule fused_schedule(int64_t M, int64_t N, int64_t K, int cus, int64_t m
   s.split = parts >= 2 && s.ntiles <= kSplitMaxTiles;
   s.parts = s.split ? parts : 1;
   s.grid = s.split ? parts * n8 : (s.ntiles < cus ? s.ntiles : cus);
+  s.band_rows = s.split ? split_band_rows(s.ntiles, s.tiles_n) : 1;
   return s;
 }
 
@@ -410,7 +416,7 @@ void launch_fused_t(const FusedGemmArgs& g, const FusedSchedule& s) {
                      (hipStream_t)g.stream, static_cast<const uint8_t*>(g.x), (uint32_t)(g.ldx * 2),
                      g.params, g.qb, (uint32_t)g.ldb, g.sb, (uint32_t)g.ldsb, (uint32_t)g.M,
                      (uint32_t)g.N, (uint32_t)g.K, g.out, (uint32_t)g.ldo, (uint32_t)s.tiles_n,
-                     (uint32_t)s.ntiles, (uint32_t)s.parts, reinterpret_cast<uint32_t*>(ws),
+                     (uint32_t)s.ntiles, (uint32_t)s.band_rows, (uint32_t)s.parts, reinterpret_cast<uint32_t*>(ws),
                      ws ? reinterpret_cast<float*>(ws + kSplitFlagBytes) : nullptr);
 }
 

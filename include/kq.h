@@ -286,8 +286,9 @@ int kq_mx_gemm_fused_ws(const void* x, int dtype, int64_t ldx, const float* para
  * through the workspace: S is the largest of 2, 4 and 8 such that S times the
  * tiles (rounded up to 8) fit on the compute units and every part has at least 5
  * K steps.  The workspace is 4096 bytes of flag words, then S x 256 KiB of fp32
- * partial sums per tile (1024 x 3072 x 12288: 48 tiles, S = 4, 48 MiB, 0.57x the
- * unsplit time).  The parts' sums are added in part order, so the result does not
+ * partial sums per tile (1024 x 3072 x 12288: 48 tiles, S = 4, 48 MiB, 0.54x the
+ * unsplit time).  Each XCD's tiles, with all their parts, form one compact block of
+ * the tile grid.  The parts' sums are added in part order, so the result does not
  * depend on the order in which they finish.  With more tiles the matrix cores are
  * already busy on most compute units and nothing is split.
  * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_HIP. */
